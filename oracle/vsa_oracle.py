@@ -1,0 +1,240 @@
+"""CPU fp64 oracle for the VSA fine block-sparse attention forward.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg import this module.  The product path (the HIP library and
+its Python binding) never imports, calls or links it, and this module imports
+nothing from the product package.
+
+What it computes, and where the pages define it:
+  * vsa_fwd -- Wan2.2 production-values dataset card, "Operator contract":
+    non-causal block-sparse attention in BSHD layout,
+    out = softmax(q . k_sel^T / sqrt(D)) . v_sel, where for each (batch, head,
+    query cube) topk_idx names the KV cubes and vbs[c] keeps only the first
+    vbs[c] of the 64 slots of cube c.
+  * vsa_preprocess -- TensorRT-Edge-LLM "Video Sparse Attention Runner",
+    preprocess entry: KC and VC are BF16 [numBlocks, numHeads, 128] block means
+    of K and block sums of V; TensorRT-LLM VisualGen VSA review snippet: the
+    mean divides the block sum by the valid count and casts to the input dtype.
+  * vsa_fwd_proxy -- the Runner's class description: in a packed
+    [prefix | video] sequence the prefix queries see all keys exactly, while a
+    64-row video query block sees the prefix, its neighbours and its chosen
+    blocks exactly and sees each remaining block only through that block's
+    averaged key and its value total.  The FlashInfer proxy-compensation
+    description on the TensorRT-LLM PR page adds: a block already computed
+    exactly is excluded from the proxy terms, and each proxy term enters the
+    softmax denominator weighted by the number of real tokens it stands for.
+
+Block-sparse attention over a key set is exact softmax attention restricted to
+that set, so the oracle is that plain definition written out in float64: the key
+set is built as a set (ascending padded slot), logits are fp64 dot products of
+the exactly widened bf16 inputs, and the softmax is the textbook
+exp(s - max) / sum form.  The graded output is the fp64 result rounded once to
+bf16 (nearest, ties to even).  Readings of points the pages leave open
+(padding rows write 0, an empty key set writes 0, indices must be distinct) are
+listed in the repository design notes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 64
+
+__all__ = ["bf16_to_f64", "f64_to_bf16", "vsa_fwd", "vsa_fwd_item", "vsa_preprocess",
+           "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots"]
+
+
+# --------------------------------------------------------------------------
+# bf16 <-> fp64
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float64 (exact: bf16 -> fp32 -> fp64)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 bit patterns in one step (nearest, ties to even).
+
+    bf16 keeps 8 significant bits, exponents down to 2^-126 for normals and a
+    quantum of 2^-133 for subnormals.  For each value the quantum is
+    2^(e - 8) with x = m * 2^e, 0.5 <= |m| < 1, floored at 2^-133; x / quantum
+    and the product back are exact in float64, and np.rint rounds half to
+    even.  Results beyond the bf16 range become +-inf; NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat = x.reshape(-1)
+    res = out.reshape(-1)
+    finite = np.isfinite(flat)
+    xf = np.where(finite, flat, 0.0)
+    _, e = np.frexp(xf)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(xf / q) * q
+    big = np.abs(r) >= 2.0 ** 128
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)
+    bits = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    sign = np.where(np.signbit(flat), np.uint16(0x8000), np.uint16(0))
+    bits = np.where(big, sign | np.uint16(0x7F80), bits)
+    bits = np.where(np.isinf(flat), sign | np.uint16(0x7F80), bits)
+    bits = np.where(np.isnan(flat), np.uint16(0x7FC0), bits)
+    res[:] = bits
+    return out
+
+
+# --------------------------------------------------------------------------
+# the plain definition, one (batch, head, query block) at a time
+# --------------------------------------------------------------------------
+def _softmax_attend(qm: np.ndarray, km: np.ndarray, vm: np.ndarray, scale: float,
+                    return_weights: bool = False):
+    """Textbook softmax attention in float64: rows of qm over the rows of km/vm."""
+    s = (qm @ km.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    w /= w.sum(axis=1, keepdims=True)
+    o = w @ vm
+    return (o, w) if return_weights else (o, None)
+
+
+def item_key_slots(blocks, vbs: np.ndarray) -> np.ndarray:
+    """Key set of one query block as ascending padded slots.
+
+    The set is {64c + t : c in blocks, t < vbs[c]}; blocks must be distinct
+    (a repeated block would count its keys twice, which the contract rules out).
+    """
+    blocks = np.asarray(blocks, dtype=np.int64).reshape(-1)
+    uniq = np.unique(blocks)
+    if uniq.size != blocks.size:
+        raise ValueError("duplicate block index in a selection row")
+    parts = [BLOCK * c + np.arange(int(vbs[c]), dtype=np.int64) for c in uniq]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def vsa_fwd_item(q, k, v, topk_idx, vbs, sm_scale, b: int, h: int, qc: int,
+                 return_weights: bool = False):
+    """fp64 output rows [vbs[qc], D] of query cube qc of head h, batch b (and weights)."""
+    vbs = np.asarray(vbs)
+    nq = int(vbs[qc])
+    D = q.shape[-1]
+    if nq == 0:
+        return (np.zeros((0, D)), np.zeros((0, 0))) if return_weights else np.zeros((0, D))
+    slots = item_key_slots(topk_idx[b, h, qc], vbs)
+    if slots.size == 0:
+        z = np.zeros((nq, D))
+        return (z, np.zeros((nq, 0))) if return_weights else z
+    qm = bf16_to_f64(q[b, BLOCK * qc:BLOCK * qc + nq, h, :])
+    km = bf16_to_f64(k[b, slots, h, :])
+    vm = bf16_to_f64(v[b, slots, h, :])
+    scale = float(np.float32(sm_scale))
+    o, w = _softmax_attend(qm, km, vm, scale, return_weights)
+    return (o, w) if return_weights else o
+
+
+def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale, items=None):
+    """fp64 forward over all items (or the listed (b, h, qc) items).
+
+    Returns o64 [B, S, H, D] float64 with padding query rows (and rows of
+    skipped items) equal to 0.  Apply f64_to_bf16 for the graded bf16 output.
+    """
+    B, S, H, D = q.shape
+    nq_blocks = S // BLOCK
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    if items is None:
+        items = [(b, h, c) for b in range(B) for h in range(H) for c in range(nq_blocks)]
+    for b, h, c in items:
+        o = vsa_fwd_item(q, k, v, topk_idx, vbs, sm_scale, b, h, c)
+        out[b, BLOCK * c:BLOCK * c + o.shape[0], h, :] = o
+    return out
+
+
+# --------------------------------------------------------------------------
+# block summaries
+# --------------------------------------------------------------------------
+def vsa_preprocess(k, v, vbs):
+    """Block summaries: kmean = bf16(sum_{t<vbs} K_t / vbs), vsum = bf16(sum_{t<vbs} V_t).
+
+    Inputs are bf16 bits [B, S, H, D]; outputs are bf16 bits [B, S/64, H, D].
+    Sums are formed in float64 (exact for bf16 data of ordinary range), divided
+    in float64 and rounded once to bf16.  A block with vbs = 0 gets zeros.
+    """
+    B, S, H, D = k.shape
+    nb = S // BLOCK
+    km = np.zeros((B, nb, H, D), np.float64)
+    vs = np.zeros((B, nb, H, D), np.float64)
+    for c in range(nb):
+        n = int(vbs[c])
+        if n == 0:
+            continue
+        rows = slice(BLOCK * c, BLOCK * c + n)
+        km[:, c] = bf16_to_f64(k[:, rows]).sum(axis=1) / n
+        vs[:, c] = bf16_to_f64(v[:, rows]).sum(axis=1)
+    return f64_to_bf16(km), f64_to_bf16(vs)
+
+
+# --------------------------------------------------------------------------
+# packed [prefix | video] proxy-compensated forward
+# --------------------------------------------------------------------------
+def vsa_fwd_proxy_item(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale,
+                       b: int, h: int, qb: int):
+    """fp64 output rows of query block qb (global block index) of head h, batch b.
+
+    Prefix query block: exact attention over every valid key, no proxies.
+    Video query block qv = qb - P/64: exact over all prefix blocks and the video
+    blocks listed in sel_idx[b, h, qv] (video-relative, -1 = empty slot); each
+    other video block c with vbs[c] > 0 adds a proxy term with logit
+    t_c = (q . kmean_c) * scale, weight vbs[c] in the denominator and exp(t_c) * vsum_c
+    in the numerator.  One common max M stabilises both sums.
+    """
+    vbs = np.asarray(vbs)
+    npb = prefix_len // BLOCK
+    nblk = vbs.size
+    nq = int(vbs[qb])
+    D = q.shape[-1]
+    if nq == 0:
+        return np.zeros((0, D))
+    scale = float(np.float32(sm_scale))
+    qm = bf16_to_f64(q[b, BLOCK * qb:BLOCK * qb + nq, h, :])
+    if qb < npb:
+        exact_blocks = list(range(nblk))
+        proxy_blocks = []
+    else:
+        sel = [int(x) for x in sel_idx[b, h, qb - npb] if x >= 0]
+        if len(set(sel)) != len(sel):
+            raise ValueError("duplicate block index in a selection row")
+        exact_blocks = list(range(npb)) + [npb + c for c in sel]
+        chosen = set(sel)
+        proxy_blocks = [npb + c for c in range(nblk - npb)
+                        if c not in chosen and int(vbs[npb + c]) > 0]
+    slots = item_key_slots(exact_blocks, vbs)
+    km = bf16_to_f64(k[b, slots, h, :])
+    vm = bf16_to_f64(v[b, slots, h, :])
+    s = (qm @ km.T) * scale                                   # exact logits
+    if proxy_blocks:
+        pk = bf16_to_f64(kmean[b, proxy_blocks, h, :])
+        pv = bf16_to_f64(vsum[b, proxy_blocks, h, :])
+        wt = vbs[proxy_blocks].astype(np.float64)
+        t = (qm @ pk.T) * scale                               # proxy logits
+        m = np.maximum(s.max(axis=1, keepdims=True), t.max(axis=1, keepdims=True))
+    else:
+        m = s.max(axis=1, keepdims=True) if s.size else np.zeros((nq, 1))
+    es = np.exp(s - m)
+    num = es @ vm
+    den = es.sum(axis=1, keepdims=True)
+    if proxy_blocks:
+        et = np.exp(t - m)
+        num = num + et @ pv
+        den = den + et @ wt[:, None]
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def vsa_fwd_proxy(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale, items=None):
+    """fp64 proxy-compensated forward over all (or the listed) (b, h, query block) items."""
+    B, S, H, D = q.shape
+    nblk = S // BLOCK
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    if items is None:
+        items = [(b, h, c) for b in range(B) for h in range(H) for c in range(nblk)]
+    for b, h, c in items:
+        o = vsa_fwd_proxy_item(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale, b, h, c)
+        out[b, BLOCK * c:BLOCK * c + o.shape[0], h, :] = o
+    return out

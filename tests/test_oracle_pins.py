@@ -1,0 +1,337 @@
+"""Pins of the CPU fp64 oracle to facts other than itself (CPU only).
+
+Each test ties the oracle to something the pages or the mathematics fix:
+brute-force textbook attention on tiny inputs, torch's float64 attention,
+closed forms, invariances, the proxy formula's exact special cases, and the
+pages' printed shapes.  A plausible slip in the oracle (a dropped scale, a
+transposed operand, the wrong cube's vbs, a mis-indexed head, a missing proxy
+weight) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_video_vsa_amd import workloads as W
+from oracle import vsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 128
+
+
+def _bf16(rng, shape, scale=1.0):
+    return W.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def _f(bits):
+    """Independent widening for tests: through torch's bfloat16 dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_f64_to_bf16_ties_and_single_rounding():
+    one = 1.0
+    cases = {
+        one: 0x3F80,
+        one + 2.0 ** -8: 0x3F80,               # tie between 1 and 1+2^-7 -> even (1)
+        one + 3 * 2.0 ** -8: 0x3F82,           # tie between m=1 and m=2 -> even (2)
+        one + 2.0 ** -8 + 2.0 ** -40: 0x3F81,  # just above the tie: fp32 double rounding would give 0x3F80
+        -2.5: 0xC020,
+        0.0: 0x0000,
+        3.3895313892515355e38: 0x7F7F,         # largest finite bf16
+        3.4e38: 0x7F80,                        # rounds past the largest finite -> inf
+        2.0 ** -133: 0x0001,                   # smallest bf16 subnormal
+        2.0 ** -134: 0x0000,                   # tie with 0 -> even (0)
+        3 * 2.0 ** -135: 0x0001,
+    }
+    xs = np.array(list(cases), dtype=np.float64)
+    got = O.f64_to_bf16(xs)
+    assert [int(g) for g in got] == list(cases.values())
+    assert O.f64_to_bf16(np.array([np.inf, -np.inf]))[0] == 0x7F80
+    assert O.f64_to_bf16(np.array([-np.inf]))[0] == 0xFF80
+
+
+def test_f64_to_bf16_matches_torch_on_float32_values():
+    # For values exactly representable in float32, torch's float32 -> bfloat16
+    # cast is a single round-to-nearest-even, so it must agree bit for bit.
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000) * 1e-39]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f64_to_bf16(x.astype(np.float64)), ref)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(_f(bits))
+    assert np.array_equal(O.bf16_to_f64(bits)[finite], _f(bits)[finite])
+
+
+# ---------------------------------------------------------------- P1 dense case
+def _dense_inputs(rng, n_cubes, H, B=1):
+    S = 64 * n_cubes
+    q, k, v = (_bf16(rng, (B, S, H, D)) for _ in range(3))
+    vbs = np.full(n_cubes, 64, np.int32)
+    topk = np.broadcast_to(np.arange(n_cubes, dtype=np.int32), (B, H, n_cubes, n_cubes)).copy()
+    return q, k, v, vbs, topk
+
+
+def test_dense_equals_bruteforce_python_loops():
+    rng = np.random.default_rng(1)
+    q, k, v, vbs, topk = _dense_inputs(rng, 2, 1)
+    scale = np.float32(1 / math.sqrt(D))
+    o = O.vsa_fwd(q, k, v, topk, vbs, scale)
+    qf, kf, vf = (_f(x)[0, :, 0, :].tolist() for x in (q, k, v))
+    sc = float(scale)
+    for i in (0, 17, 63, 64, 101, 127):
+        logits = [sc * sum(a * b for a, b in zip(qf[i], kf[j])) for j in range(128)]
+        mx = max(logits)
+        e = [math.exp(s - mx) for s in logits]
+        z = sum(e)
+        ref = [sum(e[j] * vf[j][d] for j in range(128)) / z for d in range(D)]
+        assert np.allclose(o[0, i, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_dense_equals_torch_sdpa_float64():
+    rng = np.random.default_rng(2)
+    q, k, v, vbs, topk = _dense_inputs(rng, 8, 2, B=2)
+    scale = np.float32(1 / math.sqrt(D))
+    o = O.vsa_fwd(q, k, v, topk, vbs, scale)
+    t = [torch.from_numpy(_f(x)).permute(0, 2, 1, 3) for x in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, scale=float(scale))
+    assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P2 compact dense
+def test_partial_cubes_equal_dense_attention_over_valid_tokens():
+    # topk = every cube with ragged vbs -> dense attention over the real tokens
+    # only, after mapping the padded cube-major rows back to natural order.
+    wl = W.generate("0")
+    B, S, H, _ = wl.q.shape
+    nq = S // 64
+    topk = np.broadcast_to(np.arange(nq, dtype=np.int32)[::-1], (B, H, nq, nq)).copy()
+    o = O.vsa_fwd(wl.q, wl.k, wl.v, topk, wl.vbs, wl.sm_scale)
+    slot, _ = W.tile_map(*wl.config.grid)
+    t = [torch.from_numpy(_f(x)[:, slot]).permute(0, 2, 1, 3) for x in (wl.q, wl.k, wl.v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, scale=float(wl.sm_scale))
+    assert np.allclose(o[:, slot], ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+    pad = np.ones(S, bool)
+    pad[slot] = False
+    assert np.all(o[:, pad] == 0.0)
+
+
+# ---------------------------------------------------------------- P3 order invariance
+def test_topk_order_invariance_bitwise():
+    wl = W.generate("1")
+    rng = np.random.default_rng(3)
+    perm = np.argsort(rng.random(wl.topk_idx.shape), axis=-1)
+    shuffled = np.take_along_axis(wl.topk_idx, perm, axis=-1)
+    items = [(0, h, c) for h in (0, 5) for c in range(0, 84, 7)]
+    a = O.vsa_fwd(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale, items)
+    b = O.vsa_fwd(wl.q, wl.k, wl.v, shuffled, wl.vbs, wl.sm_scale, items)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- P4 weights
+def test_softmax_weights_sum_to_one_over_valid_selected_keys():
+    wl = W.generate("1")
+    for h, c in [(0, 0), (3, 40), (7, 83)]:
+        _, w = O.vsa_fwd_item(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale, 0, h, c,
+                              return_weights=True)
+        nkeys = int(wl.vbs[wl.topk_idx[0, h, c]].sum())
+        assert w.shape == (wl.vbs[c], nkeys)
+        assert np.all(np.abs(w.sum(axis=1) - 1.0) <= 1e-14)
+        assert np.all(w >= 0)
+
+
+# ---------------------------------------------------------------- P5 pad garbage
+def test_padding_garbage_does_not_reach_valid_outputs():
+    wl = W.generate("0")
+    S = wl.q.shape[1]
+    pad = np.ones(S, bool)
+    pad[wl.valid_slots] = False
+    rng = np.random.default_rng(5)
+    q2, k2, v2 = wl.q.copy(), wl.k.copy(), wl.v.copy()
+    for x in (q2, k2, v2):
+        x[:, pad] = _bf16(rng, x[:, pad].shape, 100.0)
+    a = O.vsa_fwd(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+    b = O.vsa_fwd(q2, k2, v2, wl.topk_idx, wl.vbs, wl.sm_scale)
+    assert np.array_equal(a, b)
+    assert np.all(a[:, pad] == 0.0)
+
+
+# ---------------------------------------------------------------- P6 closed forms
+def test_closed_forms():
+    rng = np.random.default_rng(6)
+    B, H, nq = 1, 2, 4
+    S = 64 * nq
+    q, k, v = (_bf16(rng, (B, S, H, D)) for _ in range(3))
+    vbs = np.array([64, 1, 40, 64], np.int32)
+    scale = np.float32(1 / math.sqrt(D))
+    # (i) one selected cube holding one valid key -> that v row exactly
+    topk = np.full((B, H, nq, 1), 1, np.int32)
+    o = O.vsa_fwd(q, k, v, topk, vbs, scale)
+    for h in range(H):
+        for c in range(nq):
+            rows = slice(64 * c, 64 * c + vbs[c])
+            assert np.array_equal(O.f64_to_bf16(o[0, rows, h]),
+                                  np.broadcast_to(v[0, 64, h], o[0, rows, h].shape))
+    # (ii) constant V over the valid slots -> that vector
+    vc = v.copy()
+    vc[0, :, :, :] = v[0, 5, :, :][None]
+    topk2 = np.tile(np.array([0, 2], np.int32), (B, H, nq, 1))
+    o = O.vsa_fwd(q, k, vc, topk2, vbs, scale)
+    for h in range(H):
+        assert np.allclose(o[0, :64, h], _f(v)[0, 5, h][None], rtol=0, atol=1e-12)
+    # (iii) scale 0 -> arithmetic mean of the valid selected v rows
+    o = O.vsa_fwd(q, k, v, topk2, vbs, np.float32(0.0))
+    for h in range(H):
+        rows = np.concatenate([np.arange(64), 128 + np.arange(40)])
+        assert np.allclose(o[0, 64 * 3 + 7, h], _f(v)[0, rows, h].mean(axis=0), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P7 equivariance
+def test_head_and_batch_permutation_equivariance():
+    rng = np.random.default_rng(8)
+    B, H, nq, topk = 2, 3, 5, 3
+    S = 64 * nq
+    q, k, v = (_bf16(rng, (B, S, H, D)) for _ in range(3))
+    vbs = np.array([64, 12, 33, 64, 5], np.int32)
+    idx = np.argsort(rng.random((B, H, nq, nq)), axis=-1)[..., :topk].astype(np.int32)
+    scale = np.float32(0.1)
+    o = O.vsa_fwd(q, k, v, idx, vbs, scale)
+    hp, bp = np.array([2, 0, 1]), np.array([1, 0])
+    o2 = O.vsa_fwd(q[bp][:, :, hp], k[bp][:, :, hp], v[bp][:, :, hp], idx[bp][:, hp], vbs, scale)
+    assert np.array_equal(o2, o[bp][:, :, hp])
+
+
+# ---------------------------------------------------------------- P8 proxy -> exact
+def _proxy_case(rng, npb=1, video_vbs=(64, 32, 16, 64, 8, 48), H=2):
+    vbs = np.array([64] * npb + list(video_vbs), np.int32)
+    S = 64 * vbs.size
+    q, k, v = (_bf16(rng, (1, S, H, D)) for _ in range(3))
+    return q, k, v, vbs, S
+
+
+def test_proxy_with_every_block_selected_is_exact_attention():
+    rng = np.random.default_rng(9)
+    q, k, v, vbs, S = _proxy_case(rng)
+    npb, nv, H = 1, vbs.size - 1, 2
+    sel = np.broadcast_to(np.arange(nv, dtype=np.int32), (1, H, nv, nv)).copy()
+    km, vs = O.vsa_preprocess(k, v, vbs)
+    o = O.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, 64 * npb, np.float32(0.0883883))
+    full = np.broadcast_to(np.arange(vbs.size, dtype=np.int32), (1, H, vbs.size, vbs.size)).copy()
+    ref = O.vsa_fwd(q, k, v, full, vbs, np.float32(0.0883883))
+    assert np.allclose(o, ref, rtol=0, atol=1e-13)
+
+
+def test_proxy_equals_exact_when_omitted_blocks_are_summarised_exactly():
+    # In each omitted block every valid K row is the same bf16 vector, and V
+    # holds small integers, so kmean and vsum are exact in bf16 and
+    # sum_t exp(q.k_t) v_t = exp(q.kmean) * vsum, sum_t exp(q.k_t) = vbs * exp(q.kmean).
+    rng = np.random.default_rng(10)
+    q, k, v, vbs, S = _proxy_case(rng)
+    H, npb = 2, 1
+    nv = vbs.size - npb
+    for c in range(npb, vbs.size):
+        k[0, 64 * c:64 * c + vbs[c]] = k[0, 64 * c][None]
+        ints = rng.integers(-3, 4, size=(64, H, D)).astype(np.float32)
+        v[0, 64 * c:64 * c + 64] = W.f32_to_bf16_bits(ints)
+    sel = np.full((1, H, nv, 3), -1, np.int32)
+    sel[:, :, :, 0] = np.arange(nv)                  # self only
+    sel[:, 1, :, 1] = (np.arange(nv) + 2) % nv       # head 1 also picks one more
+    km, vs = O.vsa_preprocess(k, v, vbs)
+    scale = np.float32(1 / math.sqrt(D))
+    o = O.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, 64 * npb, scale)
+    full = np.broadcast_to(np.arange(vbs.size, dtype=np.int32), (1, H, vbs.size, vbs.size)).copy()
+    ref = O.vsa_fwd(q, k, v, full, vbs, scale)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+    # the proxy terms carry real mass: dropping them (exact blocks only) moves the outputs
+    exact_only = np.zeros((1, H, vbs.size, 1 + 3), np.int32) - 1
+    exact_only[..., 0] = 0
+    exact_only[:, :, npb:, 1:] = np.where(sel >= 0, sel + npb, -1)
+    for h in range(H):
+        for c in range(npb, vbs.size):
+            blocks = [int(x) for x in exact_only[0, h, c] if x >= 0]
+            slots = O.item_key_slots(blocks, vbs)
+            qm = _f(q)[0, 64 * c:64 * c + vbs[c], h]
+            s = qm @ _f(k)[0, slots, h].T * float(scale)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            part = (w / w.sum(axis=1, keepdims=True)) @ _f(v)[0, slots, h]
+            assert np.abs(part - o[0, 64 * c:64 * c + vbs[c], h]).max() > 1e-3
+
+
+def test_proxy_prefix_rows_attend_to_every_valid_key():
+    rng = np.random.default_rng(11)
+    q, k, v, vbs, S = _proxy_case(rng, npb=2)
+    H, npb = 2, 2
+    nv = vbs.size - npb
+    sel = np.full((1, H, nv, 1), -1, np.int32)
+    km, vs = O.vsa_preprocess(k, v, vbs)
+    scale = np.float32(1 / math.sqrt(D))
+    o = O.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, 64 * npb, scale)
+    slots = np.concatenate([64 * c + np.arange(vbs[c]) for c in range(vbs.size)])
+    t = [torch.from_numpy(_f(x)[:, slots]).permute(0, 2, 1, 3) for x in (q, k, v)]
+    tq = torch.from_numpy(_f(q)[:, :128]).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, t[1], t[2], scale=float(scale))
+    assert np.allclose(o[:, :128], ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P9 preprocess
+def test_preprocess_against_python_loops():
+    rng = np.random.default_rng(12)
+    H = 2
+    vbs = np.array([64, 48, 1, 0], np.int32)
+    S = 64 * vbs.size
+    k, v = _bf16(rng, (1, S, H, D), 3.0), _bf16(rng, (1, S, H, D), 3.0)
+    km, vs = O.vsa_preprocess(k, v, vbs)
+    kf, vf = _f(k), _f(v)
+    for c, n in enumerate(vbs):
+        for h in range(H):
+            for d in (0, 1, 77, 127):
+                sk = sv = 0.0
+                for t in range(int(n)):
+                    sk += kf[0, 64 * c + t, h, d]
+                    sv += vf[0, 64 * c + t, h, d]
+                mean = sk / n if n else 0.0
+                assert _f(km[0, c, h, d:d + 1])[0] == _f(O.f64_to_bf16(np.array([mean])))[0]
+                assert _f(vs[0, c, h, d:d + 1])[0] == _f(O.f64_to_bf16(np.array([sv])))[0]
+    # power-of-two counts: the mean of bf16 data is exact in float32, so torch's cast agrees
+    kk = _f(k)[0, :64].mean(axis=0).astype(np.float32)
+    ref = torch.from_numpy(kk).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(km[0, 0], ref)
+
+
+# ---------------------------------------------------------------- P10 outliers
+def test_outlier_logits_stay_finite():
+    rng = np.random.default_rng(13)
+    q, k, v, vbs, topk = _dense_inputs(rng, 2, 1)
+    qs = O.bf16_to_f64(q) * 30000.0
+    ks = O.bf16_to_f64(k) * 30000.0
+    q2, k2 = O.f64_to_bf16(qs), O.f64_to_bf16(ks)
+    o = O.vsa_fwd(q2, k2, v, topk, vbs, np.float32(1 / math.sqrt(D)))
+    assert np.all(np.isfinite(o))
+    s = (O.bf16_to_f64(q2[0, :, 0]) @ O.bf16_to_f64(k2[0, :, 0]).T)
+    assert np.abs(s).max() > 1e4
+    # a one-hot softmax returns a v row of the selected set
+    vrows = O.bf16_to_f64(v[0, :, 0])
+    assert np.min(np.abs(o[0, :, 0][:, None, :] - vrows[None]).max(axis=-1), axis=1).max() < 1e-9
+
+
+# ---------------------------------------------------------------- the pages' shapes
+def test_wan_shapes_from_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "wan_shapes.json")))
+    T, Hh, Wd = g["latent_grid"]
+    assert T * Hh * Wd == g["real_tokens"]
+    assert list(W.cube_grid(T, Hh, Wd)) == g["cube_grid"]
+    slot, vbs = W.tile_map(T, Hh, Wd)
+    assert vbs.size == g["n_cubes"] and 64 * vbs.size == g["s_padded"]
+    assert int(vbs.sum()) == g["real_tokens"]
+    assert np.unique(slot).size == slot.size and slot.max() < g["s_padded"]
+    assert np.all(slot % 64 < vbs[slot // 64])
+    cfg = W.CONFIGS["2"]
+    assert cfg.seq_len == g["s_padded"] and cfg.topk == g["topk"] and cfg.heads == g["heads"]
