@@ -1,0 +1,277 @@
+// C-ABI entry points: host-side argument checks, workspace carving and kernel
+// launches on the caller's stream.  No allocation, no synchronisation.
+#include "vsa.h"
+#include "vsa_internal.h"
+
+#include <math.h>
+
+using namespace vsa;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
+constexpr int64_t kMaxBlocks = (1 << 20) - 1;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t vt, pt, vf, pf, total;
+};
+
+// [V tiles B*H*nblk*16KB][proxy tiles B*H*nproxy*16KB][V flags][proxy flags]
+WsLayout ws_layout(int64_t batch, int64_t heads, int64_t nblk, int64_t nproxy) {
+  WsLayout l;
+  const size_t bh = (size_t)batch * (size_t)heads;
+  l.vt = 0;
+  l.pt = align_up(l.vt + bh * (size_t)nblk * kTileBytes, kWsAlign);
+  l.vf = align_up(l.pt + bh * (size_t)nproxy * kTileBytes, kWsAlign);
+  l.pf = align_up(l.vf + bh * (size_t)nblk, kWsAlign);
+  l.total = align_up(l.pf + bh * (size_t)nproxy, kWsAlign);
+  return l;
+}
+
+bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+vsa_status check_common(int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim) {
+  if (head_dim != kHeadDim) return VSA_ERR_UNSUPPORTED;
+  if (batch < 1 || num_heads < 1 || seq_len < kBlock || seq_len % kBlock != 0)
+    return VSA_ERR_SHAPE;
+  const int64_t nblk = seq_len / kBlock;
+  if (nblk > kMaxBlocks) return VSA_ERR_SHAPE;
+  if ((int64_t)batch * num_heads * nblk > (int64_t)0x7FFFFFF0) return VSA_ERR_SHAPE;
+  return VSA_OK;
+}
+
+AttnParams base_params(int32_t batch, int32_t seq_len, int32_t num_heads, float sm_scale) {
+  AttnParams p = {};
+  p.batch = batch;
+  p.seq = seq_len;
+  p.heads = num_heads;
+  p.nblk = seq_len / kBlock;
+  p.n_items = batch * num_heads * p.nblk;
+  p.items_per_xcd = (p.n_items + 7) / 8;
+  p.c = sm_scale * 1.4426950408889634f;   // log2(e): softmax evaluated with exp2
+  return p;
+}
+
+}  // namespace
+
+extern "C" const char* vsa_status_string(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_NULL: return "VSA_ERR_NULL: a required pointer is NULL";
+    case VSA_ERR_SHAPE: return "VSA_ERR_SHAPE: a size argument is out of range or inconsistent";
+    case VSA_ERR_ALIGN: return "VSA_ERR_ALIGN: a pointer is not aligned as documented";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED: head_dim must be 128";
+    case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE: workspace missing or too small";
+    case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale must be finite and >= 0";
+  }
+  return "VSA_ERR_UNKNOWN";
+}
+
+extern "C" size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
+                                         int32_t head_dim) {
+  if (check_common(batch, seq_len, num_heads, head_dim) != VSA_OK) return 0;
+  return ws_layout(batch, num_heads, seq_len / kBlock, 0).total;
+}
+
+extern "C" size_t vsa_fwd_proxy_workspace_size(int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                               int32_t num_heads, int32_t head_dim) {
+  if (check_common(batch, seq_len, num_heads, head_dim) != VSA_OK) return 0;
+  if (prefix_len <= 0 || prefix_len >= seq_len || prefix_len % kBlock != 0) return 0;
+  const int64_t nvideo = (seq_len - prefix_len) / kBlock;
+  return ws_layout(batch, num_heads, seq_len / kBlock, (nvideo + kBlock - 1) / kBlock).total;
+}
+
+namespace {
+
+// Checks shared by vsa_fwd and its two stages.
+vsa_status check_fwd(const void* q, const void* k, const void* v, const int32_t* topk_idx,
+                     const int32_t* vbs, const void* out, int32_t batch, int32_t seq_len,
+                     int32_t num_heads, int32_t head_dim, int32_t topk, float sm_scale,
+                     const void* workspace, size_t workspace_bytes, bool need_q, bool need_v) {
+  if ((need_q && (!q || !k || !topk_idx || !out)) || (need_v && !v) || !vbs) return VSA_ERR_NULL;
+  vsa_status st = check_common(batch, seq_len, num_heads, head_dim);
+  if (st != VSA_OK) return st;
+  const int nblk = seq_len / kBlock;
+  if (need_q) {
+    if (topk < 1 || topk > nblk) return VSA_ERR_SHAPE;
+    if ((size_t)topk * 8 + 16 > kMaxDynLds) return VSA_ERR_SHAPE;
+    if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
+    if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(out, 16) ||
+        !is_aligned(topk_idx, 4))
+      return VSA_ERR_ALIGN;
+  }
+  if (need_v && !is_aligned(v, 16)) return VSA_ERR_ALIGN;
+  if (!is_aligned(vbs, 4)) return VSA_ERR_ALIGN;
+  const WsLayout ws = ws_layout(batch, num_heads, nblk, 0);
+  if (!workspace || workspace_bytes < ws.total) return VSA_ERR_WORKSPACE;
+  if (!is_aligned(workspace, kWsAlign)) return VSA_ERR_ALIGN;
+  return VSA_OK;
+}
+
+vsa_status enqueue_pack(const void* v, const int32_t* vbs, int32_t batch, int32_t seq_len,
+                        int32_t num_heads, void* workspace, hipStream_t s) {
+  const int nblk = seq_len / kBlock;
+  const WsLayout ws = ws_layout(batch, num_heads, nblk, 0);
+  uint8_t* wsb = (uint8_t*)workspace;
+  PackParams pk = {};
+  pk.src = (const uint16_t*)v;
+  pk.dst = wsb + ws.vt;
+  pk.flags = wsb + ws.vf;
+  pk.vbs = vbs;
+  pk.src_rows = seq_len;
+  pk.heads = num_heads;
+  pk.tiles = nblk;
+  pk.row_offset = 0;
+  return launch_pack(pk, batch, s) == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH;
+}
+
+vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
+                          const int32_t* vbs, void* out, int32_t batch, int32_t seq_len,
+                          int32_t num_heads, int32_t topk, float sm_scale, void* workspace,
+                          hipStream_t s) {
+  const int nblk = seq_len / kBlock;
+  const WsLayout ws = ws_layout(batch, num_heads, nblk, 0);
+  uint8_t* wsb = (uint8_t*)workspace;
+  AttnParams p = base_params(batch, seq_len, num_heads, sm_scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.vt = wsb + ws.vt;
+  p.vt_flags = wsb + ws.vf;
+  p.idx = topk_idx;
+  p.vbs = vbs;
+  p.out = (uint16_t*)out;
+  p.idx_width = topk;
+  p.table_cap = topk;
+  return launch_attn(p, false, s) == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" vsa_status vsa_fwd(const void* q, const void* k, const void* v,
+                              const int32_t* topk_idx, const int32_t* vbs, void* out,
+                              int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                              int32_t topk, float sm_scale, void* workspace,
+                              size_t workspace_bytes, vsa_stream_t stream) {
+  vsa_status st = check_fwd(q, k, v, topk_idx, vbs, out, batch, seq_len, num_heads, head_dim,
+                            topk, sm_scale, workspace, workspace_bytes, true, true);
+  if (st != VSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = enqueue_pack(v, vbs, batch, seq_len, num_heads, workspace, s);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
+                        workspace, s);
+}
+
+extern "C" vsa_status vsa_pack_values(const void* v, const int32_t* vbs, int32_t batch,
+                                      int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                                      void* workspace, size_t workspace_bytes,
+                                      vsa_stream_t stream) {
+  vsa_status st = check_fwd(nullptr, nullptr, v, nullptr, vbs, nullptr, batch, seq_len, num_heads,
+                            head_dim, 1, 0.0f, workspace, workspace_bytes, false, true);
+  if (st != VSA_OK) return st;
+  return enqueue_pack(v, vbs, batch, seq_len, num_heads, workspace, (hipStream_t)stream);
+}
+
+extern "C" vsa_status vsa_fwd_prepacked(const void* q, const void* k, const int32_t* topk_idx,
+                                        const int32_t* vbs, void* out, int32_t batch,
+                                        int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                                        int32_t topk, float sm_scale, const void* workspace,
+                                        size_t workspace_bytes, vsa_stream_t stream) {
+  vsa_status st = check_fwd(q, k, nullptr, topk_idx, vbs, out, batch, seq_len, num_heads,
+                            head_dim, topk, sm_scale, workspace, workspace_bytes, true, false);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
+                        (void*)workspace, (hipStream_t)stream);
+}
+
+extern "C" vsa_status vsa_preprocess(const void* k, const void* v, const int32_t* vbs,
+                                     void* kmean, void* vsum, int32_t batch, int32_t seq_len,
+                                     int32_t num_heads, int32_t head_dim, vsa_stream_t stream) {
+  if (!k || !v || !vbs || !kmean || !vsum) return VSA_ERR_NULL;
+  vsa_status st = check_common(batch, seq_len, num_heads, head_dim);
+  if (st != VSA_OK) return st;
+  if (!is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(kmean, 16) ||
+      !is_aligned(vsum, 16) || !is_aligned(vbs, 4))
+    return VSA_ERR_ALIGN;
+  if (launch_preprocess((const uint16_t*)k, (const uint16_t*)v, vbs, (uint16_t*)kmean,
+                        (uint16_t*)vsum, batch, seq_len, num_heads,
+                        (hipStream_t)stream) != hipSuccess)
+    return VSA_ERR_LAUNCH;
+  return VSA_OK;
+}
+
+extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
+                                    const int32_t* sel_idx, const int32_t* vbs,
+                                    const void* kmean, const void* vsum, void* out,
+                                    int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                    int32_t num_heads, int32_t head_dim, int32_t max_sel,
+                                    float sm_scale, void* workspace, size_t workspace_bytes,
+                                    vsa_stream_t stream) {
+  if (!q || !k || !v || !sel_idx || !vbs || !kmean || !vsum || !out) return VSA_ERR_NULL;
+  vsa_status st = check_common(batch, seq_len, num_heads, head_dim);
+  if (st != VSA_OK) return st;
+  if (prefix_len <= 0 || prefix_len >= seq_len || prefix_len % kBlock != 0) return VSA_ERR_SHAPE;
+  const int nblk = seq_len / kBlock;
+  const int nprefix = prefix_len / kBlock;
+  const int nvideo = nblk - nprefix;
+  const int nproxy = (nvideo + kBlock - 1) / kBlock;
+  if (max_sel < 1 || max_sel > nvideo) return VSA_ERR_SHAPE;
+  const int table_cap = (nblk > nprefix + max_sel + nproxy) ? nblk : nprefix + max_sel + nproxy;
+  const size_t dyn = (size_t)table_cap * 4 + 16 + (size_t)(nprefix + max_sel + 3) * 4 +
+                     (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
+  if (dyn > kMaxDynLds) return VSA_ERR_SHAPE;
+  if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
+  if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||
+      !is_aligned(kmean, 16) || !is_aligned(vsum, 16) || !is_aligned(sel_idx, 4) ||
+      !is_aligned(vbs, 4))
+    return VSA_ERR_ALIGN;
+  const WsLayout ws = ws_layout(batch, num_heads, nblk, nproxy);
+  if (!workspace || workspace_bytes < ws.total) return VSA_ERR_WORKSPACE;
+  if (!is_aligned(workspace, kWsAlign)) return VSA_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* wsb = (uint8_t*)workspace;
+
+  PackParams pk = {};
+  pk.src = (const uint16_t*)v;
+  pk.dst = wsb + ws.vt;
+  pk.flags = wsb + ws.vf;
+  pk.vbs = vbs;
+  pk.src_rows = seq_len;
+  pk.heads = num_heads;
+  pk.tiles = nblk;
+  if (launch_pack(pk, batch, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  PackParams pp = {};
+  pp.src = (const uint16_t*)vsum;
+  pp.dst = wsb + ws.pt;
+  pp.flags = wsb + ws.pf;
+  pp.vbs = nullptr;
+  pp.src_rows = nblk;
+  pp.heads = num_heads;
+  pp.tiles = nproxy;
+  pp.row_offset = nprefix;
+  pp.valid_rows = nvideo;
+  if (launch_pack(pp, batch, s) != hipSuccess) return VSA_ERR_LAUNCH;
+
+  AttnParams p = base_params(batch, seq_len, num_heads, sm_scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.kmean = (const uint16_t*)kmean;
+  p.vt = wsb + ws.vt;
+  p.vt_flags = wsb + ws.vf;
+  p.pt = wsb + ws.pt;
+  p.pt_flags = wsb + ws.pf;
+  p.idx = sel_idx;
+  p.vbs = vbs;
+  p.out = (uint16_t*)out;
+  p.idx_width = max_sel;
+  p.nprefix = nprefix;
+  p.nvideo = nvideo;
+  p.nproxy = nproxy;
+  p.table_cap = table_cap;
+  if (launch_attn(p, true, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  return VSA_OK;
+}

@@ -1,0 +1,62 @@
+// Internal declarations shared by the host entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vsa {
+
+constexpr int kBlock = 64;       // tokens per cube / block
+constexpr int kHeadDim = 128;    // head geometry fixed at compile time
+constexpr int kTileBytes = kBlock * kHeadDim * 2;   // one 64 x 128 16-bit tile
+
+// ---- packed V tiles ------------------------------------------------------
+// Each (batch, head, tile) V^T tile is 16 KB: two 8 KB key halves (keys 0-31,
+// 32-63); inside a half, 128 rows (one per head-dim index d) of 32 keys = 64 B,
+// split in four 16 B chunks that are XOR-swizzled by vt_swizzle(d); inside a
+// chunk the eight keys follow the MFMA k-slot order (see vsa_attn.hip).
+// Elements are fp16 when the tile's values fit fp16 well, else bf16 (flag 1).
+__host__ __device__ inline int vt_swizzle(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+
+struct PackParams {
+  const uint16_t* src;      // bf16 BSHD source rows
+  uint8_t* dst;             // packed tiles
+  uint8_t* flags;           // one byte per tile: 0 fp16, 1 bf16
+  const int32_t* vbs;       // per-block valid rows (block-indexed mode) or nullptr
+  int64_t src_rows;         // rows per batch in src
+  int heads;
+  int tiles;                // tiles per (batch, head)
+  int row_offset;           // first source row of tile 0 (in rows)
+  int valid_rows;           // proxy mode: rows [0, valid_rows) after row_offset are valid
+};
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* kmean;    // proxy mode
+  const uint8_t* vt;        // packed V tiles [B][H][nblk]
+  const uint8_t* vt_flags;
+  const uint8_t* pt;        // packed vsum tiles [B][H][nproxy] (proxy mode)
+  const uint8_t* pt_flags;
+  const int32_t* idx;       // topk_idx [B,H,Nq,topk] or sel_idx [B,H,Nv,max_sel]
+  const int32_t* vbs;
+  uint16_t* out;
+  int batch, seq, heads, nblk;
+  int idx_width;            // topk or max_sel
+  int nprefix;              // prefix blocks (proxy mode)
+  int nvideo;               // video blocks (proxy mode)
+  int nproxy;               // proxy tiles of 64 video blocks (proxy mode)
+  int n_items;              // batch * heads * nblk
+  int items_per_xcd;
+  int table_cap;            // tile-table capacity (entries)
+  float c;                  // sm_scale * log2(e)
+};
+
+hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream);
+hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t* vbs,
+                             uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
+                             hipStream_t stream);
+hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+
+}  // namespace vsa

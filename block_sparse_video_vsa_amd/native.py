@@ -1,0 +1,243 @@
+"""ctypes binding of libvsa.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind include/vsa.h;
+this module checks tensor dtypes, devices and shapes, hands raw device
+pointers and the current HIP stream to the C ABI, and turns a non-OK status
+into VSAError.  There is no fallback path: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "vsa.h")
+BLOCK = 64
+HEAD_DIM = 128
+
+_lib = None
+_lock = threading.Lock()
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_size_t = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+# (name, restype, argtypes)
+_SIGNATURES = {
+    "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "vsa_fwd_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
+    "vsa_fwd": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+    "vsa_pack_values": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p,
+                                       _size_t, _c_void_p]),
+    "vsa_fwd_prepacked": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t,
+                                         _c_void_p]),
+    "vsa_preprocess": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _i32, _i32, _i32, _i32, _c_void_p]),
+    "vsa_fwd_proxy_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32]),
+    "vsa_fwd_proxy": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+}
+
+VSA_OK = 0
+
+
+class VSAError(RuntimeError):
+    """A libvsa call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)}")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libvsa.so (raises ImportError if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().vsa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != VSA_OK:
+        raise VSAError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _default_scale(sm_scale):
+    return 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+
+
+# workspace cache: one buffer per (device, bytes), reused by later calls
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = (device, nbytes)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _ws_cache.clear()
+        _ws_cache[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
+def fwd_workspace_size(batch: int, seq_len: int, heads: int, head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().vsa_fwd_workspace_size(batch, seq_len, heads, head_dim))
+
+
+def proxy_workspace_size(batch: int, seq_len: int, prefix_len: int, heads: int,
+                         head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().vsa_fwd_proxy_workspace_size(batch, seq_len, prefix_len, heads,
+                                                           head_dim))
+
+
+def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale=None, out=None, workspace=None):
+    """Fine block-sparse attention forward (C ABI vsa_fwd) on q's device and current stream.
+
+    q, k, v: bf16 [B, S, H, 128]; topk_idx: int32 [B, H, S/64, topk]; vbs: int32 [S/64].
+    Returns out (bf16 [B, S, H, 128]).
+    """
+    lib = load_library()
+    dev = q.device
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev, (B, S, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    if topk_idx.dim() != 4 or tuple(topk_idx.shape[:3]) != (B, H, S // BLOCK):
+        raise ValueError(f"topk_idx has shape {tuple(topk_idx.shape)}, expected (B, H, S/64, topk)")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev, (B, S, H, D))
+    nbytes = fwd_workspace_size(B, S, H, D)
+    if workspace is None:
+        workspace = _workspace(dev, max(nbytes, 1))
+    st = lib.vsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S, H, D,
+                     topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
+                     workspace.numel(), _stream(dev))
+    _check("vsa_fwd", st)
+    return out
+
+
+def vsa_pack_values(v, vbs, workspace):
+    """First stage of vsa_fwd: packed V tiles into workspace (uint8 device tensor)."""
+    lib = load_library()
+    dev = v.device
+    B, S, H, D = v.shape
+    _need(v, "v", torch.bfloat16, dev)
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    st = lib.vsa_pack_values(_ptr(v), _ptr(vbs), B, S, H, D, _ptr(workspace), workspace.numel(),
+                             _stream(dev))
+    _check("vsa_pack_values", st)
+
+
+def vsa_fwd_prepacked(q, k, topk_idx, vbs, workspace, sm_scale=None, out=None):
+    """Second stage of vsa_fwd: attention over a workspace filled by vsa_pack_values."""
+    lib = load_library()
+    dev = q.device
+    B, S, H, D = q.shape
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k, "k", torch.bfloat16, dev, (B, S, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.vsa_fwd_prepacked(_ptr(q), _ptr(k), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S, H,
+                               D, topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
+                               workspace.numel(), _stream(dev))
+    _check("vsa_fwd_prepacked", st)
+    return out
+
+
+def vsa_preprocess(k, v, vbs, kmean=None, vsum=None):
+    """Block summaries (C ABI vsa_preprocess): returns (kmean, vsum), bf16 [B, S/64, H, 128]."""
+    lib = load_library()
+    dev = k.device
+    B, S, H, D = k.shape
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev, (B, S, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    shape = (B, S // BLOCK, H, D)
+    if kmean is None:
+        kmean = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    if vsum is None:
+        vsum = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(kmean, "kmean", torch.bfloat16, dev, shape)
+    _need(vsum, "vsum", torch.bfloat16, dev, shape)
+    st = lib.vsa_preprocess(_ptr(k), _ptr(v), _ptr(vbs), _ptr(kmean), _ptr(vsum), B, S, H, D,
+                            _stream(dev))
+    _check("vsa_preprocess", st)
+    return kmean, vsum
+
+
+def vsa_fwd_proxy(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale=None, out=None,
+                  workspace=None):
+    """Packed [prefix | video] proxy-compensated forward (C ABI vsa_fwd_proxy)."""
+    lib = load_library()
+    dev = q.device
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev, (B, S, H, D))
+    nblk = S // BLOCK
+    _need(vbs, "vbs", torch.int32, dev, (nblk,))
+    _need(kmean, "kmean", torch.bfloat16, dev, (B, nblk, H, D))
+    _need(vsum, "vsum", torch.bfloat16, dev, (B, nblk, H, D))
+    _need(sel_idx, "sel_idx", torch.int32, dev)
+    nv = (S - prefix_len) // BLOCK
+    if sel_idx.dim() != 4 or tuple(sel_idx.shape[:3]) != (B, H, nv):
+        raise ValueError(f"sel_idx has shape {tuple(sel_idx.shape)}, expected (B, H, Nv, max_sel)")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev, (B, S, H, D))
+    nbytes = proxy_workspace_size(B, S, prefix_len, H, D)
+    if workspace is None:
+        workspace = _workspace(dev, max(nbytes, 1))
+    st = lib.vsa_fwd_proxy(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(vbs), _ptr(kmean),
+                           _ptr(vsum), _ptr(out), B, S, prefix_len, H, D, sel_idx.shape[3],
+                           _default_scale(sm_scale), _ptr(workspace), workspace.numel(),
+                           _stream(dev))
+    _check("vsa_fwd_proxy", st)
+    return out

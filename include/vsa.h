@@ -1,0 +1,172 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) Video Sparse Attention forward library.
+ *
+ * The library computes the fine block-sparse attention stage of Video Sparse
+ * Attention (VSA).  Definitions it follows (cited by page title and section):
+ *
+ *   [OC]  Wan2.2 production-values dataset card, "Operator contract": non-causal
+ *         block-sparse attention in BSHD layout, out = softmax(q k_sel^T / sqrt(D)) v_sel;
+ *         for each (batch, head, query cube) topk_idx names the selected KV cubes
+ *         and vbs[c] keeps only the first vbs[c] of the 64 slots of cube c.
+ *   [SH]  same card, "Shapes": 64-token cubes, D = 128, sm_scale = 1/sqrt(128).
+ *   [RUN] TensorRT-Edge-LLM "Video Sparse Attention Runner": the preprocess entry
+ *         (BF16 [numBlocks, numHeads, 128] block means of K and block sums of V),
+ *         the packed [prefix | video] proxy forward, status-by-return calls that
+ *         run asynchronously on a caller stream with a caller-owned workspace.
+ *   [PX]  FlashInfer proxy-compensation description on the TensorRT-LLM VisualGen
+ *         VSA PR page: an omitted block is represented by one averaged key and one
+ *         value total; exactly computed blocks get no proxy; each proxy term is
+ *         weighted in the softmax denominator by the real tokens it represents.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are caller-owned DEVICE memory on the current HIP device.  The
+ *     library never allocates, frees, synchronises or logs.
+ *   - q, k, v, out, kmean, vsum: bf16, BSHD [batch, rows, heads, 128], contiguous,
+ *     16-byte aligned.  Index and vbs arrays: int32, contiguous, 4-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  A
+ *     call returns after enqueueing; results are ready when the stream is.
+ *   - Host-side argument checks run before anything is enqueued; on error
+ *     nothing is enqueued and the status says why.  Data preconditions (indices
+ *     in range and distinct per row, 0 <= vbs <= 64) are NOT checked on the
+ *     device: an out-of-range index is skipped, a repeated index is counted twice.
+ *   - Calls that share a workspace must not overlap in time.
+ *   - Only head_dim == 128 is supported ([SH]; the head geometry is fixed at
+ *     compile time, as in [RUN]).
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (HIP declares it as a pointer to this struct). */
+struct ihipStream_t;
+typedef struct ihipStream_t* vsa_stream_t;
+
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_NULL = 1,        /* a required pointer is NULL                           */
+  VSA_ERR_SHAPE = 2,       /* a size argument is out of range or inconsistent     */
+  VSA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented              */
+  VSA_ERR_UNSUPPORTED = 4, /* head_dim != 128                                     */
+  VSA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch            */
+  VSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
+  VSA_ERR_VALUE = 7        /* sm_scale negative, NaN or infinite                  */
+} vsa_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* vsa_status_string(vsa_status s);
+
+/*
+ * Workspace bytes vsa_fwd needs for this shape (0 if the shape is invalid).
+ * The workspace holds each (batch, head, cube) V tile transposed to key-major
+ * half precision, plus one byte per tile; it is fully rewritten by every call.
+ */
+size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
+                              int32_t head_dim);
+
+/*
+ * vsa_fwd -- fine block-sparse attention forward ([OC]).
+ *
+ *   q, k, v       bf16 [batch, seq_len, num_heads, head_dim], cube-major tiled:
+ *                 rows 64c .. 64c+63 form cube c.
+ *   topk_idx      int32 [batch, num_heads, seq_len/64, topk]: selected KV cubes
+ *                 of each (batch, head, query cube); any order (the result does
+ *                 not depend on it).
+ *   vbs           int32 [seq_len/64]: valid rows of each cube, shared by all
+ *                 batches and heads; rows >= vbs[c] are padding on both the
+ *                 query and the key side.
+ *   out           bf16 [batch, seq_len, num_heads, head_dim], written in full:
+ *                 valid query rows get softmax(q k^T * sm_scale) v over the valid
+ *                 rows of the selected cubes (rounded to nearest-even bf16);
+ *                 padding rows, rows with no valid key and non-finite results get 0.
+ *   sm_scale      finite, >= 0 (the pages use 1/sqrt(128)).
+ *   workspace     device memory of at least vsa_fwd_workspace_size(...) bytes,
+ *                 256-byte aligned.
+ *
+ * Returns VSA_OK, or the error that stopped the call before enqueueing.
+ */
+vsa_status vsa_fwd(const void* q, const void* k, const void* v,
+                   const int32_t* topk_idx, const int32_t* vbs, void* out,
+                   int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                   int32_t topk, float sm_scale,
+                   void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+
+/*
+ * The two stages of vsa_fwd, for callers that time or schedule them apart.
+ *
+ * vsa_pack_values writes the packed V tiles of (v, vbs) into the workspace
+ * (what vsa_fwd does first); vsa_fwd_prepacked runs the attention on a
+ * workspace that vsa_pack_values filled for the same v, vbs and shape (what
+ * vsa_fwd does second).  Arguments have the meaning given for vsa_fwd.
+ * Running vsa_pack_values then vsa_fwd_prepacked on one stream gives exactly
+ * the result of vsa_fwd.
+ */
+vsa_status vsa_pack_values(const void* v, const int32_t* vbs,
+                           int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                           void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+
+vsa_status vsa_fwd_prepacked(const void* q, const void* k, const int32_t* topk_idx,
+                             const int32_t* vbs, void* out,
+                             int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                             int32_t topk, float sm_scale,
+                             const void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+
+/*
+ * vsa_preprocess -- block summaries ([RUN] preprocess entry; [PX]).
+ *
+ *   k, v          bf16 [batch, seq_len, num_heads, head_dim].
+ *   vbs           int32 [seq_len/64].
+ *   kmean, vsum   bf16 [batch, seq_len/64, num_heads, head_dim] outputs:
+ *                 kmean[b,c,h,:] = bf16(sum_{t<vbs[c]} k[b,64c+t,h,:] / vbs[c]),
+ *                 vsum [b,c,h,:] = bf16(sum_{t<vbs[c]} v[b,64c+t,h,:]);
+ *                 sums in float64, one rounding to nearest-even bf16;
+ *                 vbs[c] == 0 gives zeros.
+ */
+vsa_status vsa_preprocess(const void* k, const void* v, const int32_t* vbs,
+                          void* kmean, void* vsum,
+                          int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                          vsa_stream_t stream);
+
+/* Workspace bytes vsa_fwd_proxy needs for this shape (0 if the shape is invalid). */
+size_t vsa_fwd_proxy_workspace_size(int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                    int32_t num_heads, int32_t head_dim);
+
+/*
+ * vsa_fwd_proxy -- packed [prefix | video] proxy-compensated forward ([RUN]; [PX]).
+ *
+ *   q, k, v       bf16 [batch, seq_len, num_heads, head_dim]; rows < prefix_len
+ *                 are the dense prefix, the rest are cube-major video rows.
+ *   prefix_len    multiple of 64 with 0 < prefix_len < seq_len.
+ *   vbs           int32 [seq_len/64] for every block (prefix blocks normally 64).
+ *   sel_idx       int32 [batch, num_heads, (seq_len-prefix_len)/64, max_sel]:
+ *                 video-relative block ids attended exactly by each video query
+ *                 block (normally itself, its face neighbours and the routed
+ *                 blocks); -1 marks an empty slot.
+ *   kmean, vsum   bf16 [batch, seq_len/64, num_heads, head_dim] block summaries
+ *                 (as written by vsa_preprocess).
+ *   out           bf16 [batch, seq_len, num_heads, head_dim], written in full.
+ *
+ * A prefix query row attends exactly to every valid key.  A video query row in
+ * video block qv attends exactly to the valid keys of all prefix blocks and of
+ * the blocks in sel_idx[b,h,qv,:]; every other video block c with vbs > 0 adds a
+ * proxy term: logit t = (q . kmean_c) * sm_scale, exp(t) * vsum_c to the
+ * numerator and exp(t) * vbs[c] to the denominator.
+ */
+vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
+                         const int32_t* sel_idx, const int32_t* vbs,
+                         const void* kmean, const void* vsum, void* out,
+                         int32_t batch, int32_t seq_len, int32_t prefix_len,
+                         int32_t num_heads, int32_t head_dim, int32_t max_sel,
+                         float sm_scale, void* workspace, size_t workspace_bytes,
+                         vsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

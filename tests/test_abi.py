@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/vsa.h declares, and rejects bad arguments on the host before any
+device work (so these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_video_vsa_amd import native
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vsa.h")
+OK, NULL, SHAPE, ALIGN, UNSUP, LAUNCH, WS, VALUE = range(8)
+FAKE = 0x10000          # a non-null, 256-byte-aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(vsa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return native.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"vsa_fwd", "vsa_preprocess", "vsa_fwd_proxy", "vsa_status_string",
+            "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
+            "vsa_fwd_prepacked"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(native._SIGNATURES) == set(names)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert native.status_string(s).startswith("VSA_")
+    assert native.status_string(99) == "VSA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    # 16 KB packed V tile + one flag byte per (batch, head, cube), 256-byte aligned regions
+    n = native.fwd_workspace_size(1, 39936, 40)
+    assert n == 40 * 624 * 16384 + ((40 * 624 + 255) // 256) * 256
+    assert native.fwd_workspace_size(2, 512, 2) >= 2 * 2 * 8 * 16384 + 32
+    assert native.fwd_workspace_size(1, 100, 2) == 0
+    assert native.fwd_workspace_size(1, 512, 2, 64) == 0
+    assert native.proxy_workspace_size(1, 40448, 512, 56) > native.fwd_workspace_size(1, 40448, 56)
+    assert native.proxy_workspace_size(1, 40448, 0, 56) == 0
+    assert native.proxy_workspace_size(1, 40448, 100, 56) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, vbs=FAKE, out=FAKE, B=1, S=512, H=2, D=128, topk=2,
+             scale=0.088, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.vsa_fwd(a["q"], a["k"], a["v"], a["idx"], a["vbs"], a["out"], a["B"], a["S"], a["H"],
+                       a["D"], a["topk"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_fwd_rejects_bad_arguments_on_host(lib):
+    assert _fwd(lib, q=None) == NULL
+    assert _fwd(lib, vbs=None) == NULL
+    assert _fwd(lib, D=64) == UNSUP
+    assert _fwd(lib, S=100) == SHAPE
+    assert _fwd(lib, S=0) == SHAPE
+    assert _fwd(lib, B=0) == SHAPE
+    assert _fwd(lib, H=0) == SHAPE
+    assert _fwd(lib, topk=0) == SHAPE
+    assert _fwd(lib, topk=9) == SHAPE
+    assert _fwd(lib, scale=-1.0) == VALUE
+    assert _fwd(lib, scale=float("nan")) == VALUE
+    assert _fwd(lib, scale=float("inf")) == VALUE
+    assert _fwd(lib, q=FAKE + 8) == ALIGN
+    assert _fwd(lib, idx=FAKE + 2) == ALIGN
+    assert _fwd(lib, ws=None) == WS
+    assert _fwd(lib, wsb=1000) == WS
+    assert _fwd(lib, ws=FAKE + 16) == ALIGN
+
+
+def test_stage_and_proxy_entry_points_reject_bad_arguments(lib):
+    assert lib.vsa_pack_values(None, FAKE, 1, 512, 2, 128, FAKE, 1 << 30, None) == NULL
+    assert lib.vsa_pack_values(FAKE, FAKE, 1, 512, 2, 128, FAKE, 10, None) == WS
+    assert lib.vsa_fwd_prepacked(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, 0, 0.1, FAKE,
+                                 1 << 30, None) == SHAPE
+    assert lib.vsa_preprocess(FAKE, FAKE, FAKE, FAKE, None, 1, 512, 2, 128, None) == NULL
+    assert lib.vsa_preprocess(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 96, None) == UNSUP
+    assert lib.vsa_preprocess(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, None) == ALIGN
+    px = lambda **kw: lib.vsa_fwd_proxy(  # noqa: E731
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, kw.get("S", 1024), kw.get("P", 128),
+        2, 128, kw.get("sel", 4), kw.get("scale", 0.1), FAKE, kw.get("wsb", 1 << 30), None)
+    assert px(P=0) == SHAPE
+    assert px(P=1024) == SHAPE
+    assert px(P=100) == SHAPE
+    assert px(sel=0) == SHAPE
+    assert px(sel=15) == SHAPE
+    assert px(scale=-2.0) == VALUE
+    assert px(wsb=100) == WS
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 1, 1, 1, dtype=torch.int32)
+    vbs = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises((ValueError, TypeError, RuntimeError, AssertionError)):
+        native.vsa_fwd(q, q, q, idx, vbs, out=q)
