@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--config", default="2")
     ap.add_argument("--cpu-items", type=int, default=4000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run plain device copies of this many MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -84,6 +87,15 @@ def main():
         sys.exit(1)
     vsa.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        x = torch.ones(n, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(max(args.steps, 1)):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration_mib} MiB x {max(args.steps, 1)}")
+        return
     cfg = W.CONFIGS[args.config]
     if cfg.proxy:
         log("the headline benchmark uses a plain (non-proxy) configuration")

@@ -51,6 +51,9 @@ AttnParams base_params(int32_t batch, int32_t seq_len, int32_t num_heads, float 
   p.nblk = seq_len / kBlock;
   p.n_items = batch * num_heads * p.nblk;
   p.items_per_xcd = (p.n_items + 7) / 8;
+  // 32 CUs per XCD x 4 resident workgroups per CU (two wave64s each, 256 VGPRs,
+  // about 33 KB of LDS)
+  p.phase_slots = 128;
   p.c = sm_scale * 1.4426950408889634f;   // log2(e): softmax evaluated with exp2
   return p;
 }

@@ -443,6 +443,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     wg_barrier();
     nexact = sm.cnt[0];
   }
+  // Phase-aligned sweep: the exact tiles are processed in ascending block order
+  // starting at block `start` and wrapping around.  Workgroups run on an XCD in
+  // dispatch-slot order and take about the same time, so giving slot n the start
+  // n * nblk / phase_slots (phase_slots = workgroups resident per XCD) keeps all
+  // resident workgroups of a head near the same blocks at the same moment: the
+  // XCD's L2 then serves a narrow window of that head's K/V instead of all of it.
+  // The order does not change the result beyond rounding.
+  int rot = 0;
+  {
+    const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.phase_slots) % p.nblk);
+    for (int c0 = 0; c0 < nexact; c0 += 64) {
+      const int t = c0 + lane;
+      const bool before = t < nexact && ent_id(sm.tab[t]) < start;
+      rot += __popcll(__ballot(before));
+    }
+  }
   int ntiles = nexact;
   if (kProxy && !prefix_item) {
     // proxy tiles; per proxy key (one per video block) the denominator weight
@@ -527,15 +543,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else issue_v<8>(v_src(e), 8192 * w, vlane, sV);
   };
 
+  auto tab_at = [&](int j) -> int {
+    int jj = j;
+    if (j < nexact) {
+      jj = j + rot;
+      if (jj >= nexact) jj -= nexact;
+    }
+    return __builtin_amdgcn_readfirstlane(sm.tab[jj]);
+  };
+
   if (ntiles > 0) {
-    const int e0 = __builtin_amdgcn_readfirstlane(sm.tab[0]);
+    const int e0 = tab_at(0);
     issue_tile_k(e0);
     issue_tile_v(e0);
   }
 
   for (int j = 0; j < ntiles; ++j) {
-    const int e = __builtin_amdgcn_readfirstlane(sm.tab[j]);
-    const int en = (j + 1 < ntiles) ? __builtin_amdgcn_readfirstlane(sm.tab[j + 1]) : 0;
+    const int e = tab_at(j);
+    const int en = (j + 1 < ntiles) ? tab_at(j + 1) : 0;
     const int nv = ent_nv(e);
     const bool half = nv <= 32;
     const int mode = (kProxy && (e & kEntProxy)) ? kModeProxy : ((nv & 31) ? kModePartial : kModeFull);

@@ -50,6 +50,7 @@ struct AttnParams {
   int n_items;              // batch * heads * nblk
   int items_per_xcd;
   int table_cap;            // tile-table capacity (entries)
+  int phase_slots;          // workgroups resident per XCD (sweep phase period)
   float c;                  // sm_scale * log2(e)
 };
 
