@@ -101,7 +101,7 @@ vsa_status check_fwd(const void* q, const void* k, const void* v, const int32_t*
   const int nblk = seq_len / kBlock;
   if (need_q) {
     if (topk < 1 || topk > nblk) return VSA_ERR_SHAPE;
-    if ((size_t)topk * 8 + 16 > kMaxDynLds) return VSA_ERR_SHAPE;
+    if ((size_t)topk * 12 > kMaxDynLds) return VSA_ERR_SHAPE;
     if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
     if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(out, 16) ||
         !is_aligned(topk_idx, 4))
@@ -224,8 +224,7 @@ extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
   const int nproxy = (nvideo + kBlock - 1) / kBlock;
   if (max_sel < 1 || max_sel > nvideo) return VSA_ERR_SHAPE;
   const int table_cap = (nblk > nprefix + max_sel + nproxy) ? nblk : nprefix + max_sel + nproxy;
-  const size_t dyn = (size_t)table_cap * 4 + 16 + (size_t)(nprefix + max_sel + 3) * 4 +
-                     (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
+  const size_t dyn = (size_t)table_cap * 12 + (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
   if (dyn > kMaxDynLds) return VSA_ERR_SHAPE;
   if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
   if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||

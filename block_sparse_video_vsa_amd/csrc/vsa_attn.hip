@@ -6,8 +6,8 @@
 // cube c.  The proxy variant (TensorRT-Edge-LLM "Video Sparse Attention Runner"
 // class description; FlashInfer proxy-compensation description on the
 // TensorRT-LLM VisualGen VSA PR page) adds, for every unselected video block,
-// one key (the block's mean key) whose probability is weighted by the block's
-// valid-row count and whose value is the block's value total.
+// one key (the block's mean key) whose value is the block's value total and
+// whose probability counts vbs times in the softmax denominator.
 //
 // Work decomposition: one workgroup of two wave64s per (batch, head, query
 // block); wave w owns query rows 32w..32w+31.  For each selected KV tile:
@@ -29,6 +29,11 @@
 // from the packed key-major copy written by pack_vt_kernel, which already has
 // the LDS layout, so their copy is linear.  Tiles whose vbs is <= 32 load and
 // multiply only their first 32 keys.
+//
+// Tiles are processed grouped by kind (full, full with padding keys, half, half
+// with padding keys, proxy, bf16), each kind by a straight-line specialisation
+// of the tile step, so the accumulators never cross data-dependent control flow
+// except the rescale.
 #include "vsa_internal.h"
 
 #include <math.h>
@@ -39,7 +44,6 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(2))) short s16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -48,8 +52,8 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr int kThreads = 128;
 // Between two rescales the running maximum may lag the true one by up to this
-// many log2 units, so probabilities stay below 2^8 (exact in fp16's range) while
-// most tiles skip the accumulator rescale.
+// many log2 units, so probabilities stay below 2^8 (well inside fp16's range)
+// while tiles whose maximum grew only a little skip the accumulator rescale.
 constexpr float kRescaleSlack = 8.0f;
 
 // Tile-table entry: block/tile id (bits 0-19), valid rows (20-26), bf16 V (27),
@@ -57,9 +61,25 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kEntNvShift = 20;
 constexpr int kEntBf16 = 1 << 27;
 constexpr int kEntProxy = 1 << 28;
-
 __device__ inline int ent_id(int e) { return e & 0xFFFFF; }
 __device__ inline int ent_nv(int e) { return (e >> kEntNvShift) & 127; }
+// Half tiles (exact fp16 tiles with vbs <= 32) load and multiply 32 keys only.
+__device__ inline bool ent_half(int e) { return !(e & (kEntBf16 | kEntProxy)) && ent_nv(e) <= 32; }
+
+// Tile kinds, processed in this order.
+enum : int { kGFull = 0, kGFullPad, kGHalf, kGHalfPad, kGProxy, kGBf16, kGroups };
+__device__ inline int ent_group(int e) {
+  if (e & kEntBf16) return kGBf16;
+  if (e & kEntProxy) return kGProxy;
+  const int nv = ent_nv(e);
+  if (nv == 64) return kGFull;
+  if (nv > 32) return kGFullPad;
+  if (nv == 32) return kGHalf;
+  return kGHalfPad;
+}
+
+// Softmax variants of a tile step.
+enum : int { kModeFull = 0, kModePad = 1, kModeProxy = 2, kModeAny = 3 };
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -129,17 +149,6 @@ __device__ inline unsigned pack_bf16(float p0, float p1, float& lsum) {
   return a | (b << 16);
 }
 
-struct Smem {
-  unsigned char* k;     // 16 KB K tile
-  unsigned char* v;     // 16 KB packed V tile
-  int* tab;             // tile table
-  int* cnt;             // counters
-  int* key;             // sort keys
-  float* off;           // proxy logit offsets (log2 weight or -inf)
-  float* wt;            // proxy denominator weights (valid rows, 0 = no key)
-  unsigned* bits;       // proxy selected-block bitmask
-};
-
 // Issue the global->LDS copies of one tile's K rows: N instructions of four
 // rows each starting at row r0 (full tiles: wave w copies rows 32w..32w+31 with
 // N = 8; half tiles: rows 16w..16w+15 with N = 4).  Lane l brings row
@@ -186,10 +195,6 @@ __device__ inline void issue_v(const uint8_t* vtile, int base, uint32_t vlane, u
   }
 }
 
-constexpr int kModeFull = 0;     // every key of the loaded halves is valid
-constexpr int kModePartial = 1;  // keys >= nv are padding
-constexpr int kModeProxy = 2;    // per-key log2 weights (-inf = no key)
-
 // S^T (NKB x 32 keys, 32 queries) = K . Q^T.  Register i of s[kb] in lane
 // (ln, hh) is key 32kb + 8(i/4) + 4hh + (i%4) against query ln.
 template <int NKB>
@@ -209,32 +214,33 @@ __device__ inline void s_tile(const unsigned char* sk, const bf16x8 (&qop)[8], i
   }
 }
 
+__device__ inline int key_of(int kb, int i, int hh) { return 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// Per-wave running state of one item.
+struct State {
+  f32x16 o0, o1, o2, o3;   // O^T accumulators, d blocks 0..3
+  float mc;                // running max of the scaled logits (log2 units)
+  float lsum;              // this lane's share of the softmax denominator
+};
+
 // Running-max update for one tile: the tile's largest logit (scaled, log2
 // units), and a rescale of O and the row sum when it exceeds the running max
-// by more than kRescaleSlack.  Returns false when the tile has no live key.
-template <int NKB>
-__device__ inline bool tile_max(const f32x16 (&s)[2], int mode, int nv, const float* offs,
-                                float c, int hh, float& mc, float& lsum, f32x16& o0, f32x16& o1,
-                                f32x16& o2, f32x16& o3) {
+// by more than kRescaleSlack.
+template <int NKB, int MODE>
+__device__ inline void tile_max(const f32x16 (&s)[2], int nv, const float* offs, float c, int hh,
+                                State& st) {
   float t = -INFINITY;
-  if (mode == kModeProxy) {
+  if (MODE == kModeProxy) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        t = fmaxf(t, fmaf(s[kb][i], c, offs[key]));
-      }
+      for (int i = 0; i < 16; ++i) t = fmaxf(t, fmaf(s[kb][i], c, offs[key_of(kb, i, hh)]));
     t = pair_max(t);
-    if (__ballot(t > -INFINITY) == 0ull) return false;
-  } else if (mode == kModePartial) {
+  } else if (MODE == kModePad) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        t = fmaxf(t, key < nv ? s[kb][i] : -INFINITY);
-      }
+      for (int i = 0; i < 16; ++i) t = fmaxf(t, key_of(kb, i, hh) < nv ? s[kb][i] : -INFINITY);
     t = pair_max(t) * c;
   } else {
 #pragma unroll
@@ -243,18 +249,17 @@ __device__ inline bool tile_max(const f32x16 (&s)[2], int mode, int nv, const fl
       for (int i = 0; i < 16; ++i) t = fmaxf(t, s[kb][i]);
     t = pair_max(t) * c;
   }
-  const bool trig = t > mc + kRescaleSlack;
+  const bool trig = t > st.mc + kRescaleSlack;
   if (__ballot(trig) != 0ull) {
-    const float mnew = trig ? t : mc;
-    const float alpha = __builtin_amdgcn_exp2f(mc - mnew);
-    mc = mnew;
-    lsum *= alpha;
-    o0 *= alpha;
-    o1 *= alpha;
-    o2 *= alpha;
-    o3 *= alpha;
+    const float mnew = trig ? t : st.mc;
+    const float alpha = __builtin_amdgcn_exp2f(st.mc - mnew);
+    st.mc = mnew;
+    st.lsum *= alpha;
+    st.o0 *= alpha;
+    st.o1 *= alpha;
+    st.o2 *= alpha;
+    st.o3 *= alpha;
   }
-  return true;
 }
 
 // Probabilities of one 32-key half (register i = key 32kb + 8(i/4) + 4hh + i%4)
@@ -262,25 +267,16 @@ __device__ inline bool tile_max(const f32x16 (&s)[2], int mode, int nv, const fl
 // values the MFMA multiplies.  A proxy key stands for a whole block: its value
 // operand is the block's value total, so the numerator takes its probability
 // as is and only the denominator multiplies it by the block's valid-row count.
-__device__ inline void half_probs(const f32x16& sk, int kb, int mode, int nv, const float* offs,
-                                  const float* wts, bool bf16, float c, float nmc, int hh,
-                                  float& lsum, unsigned (&pk)[8]) {
-  auto emit = [&](auto prob) {
-    if (bf16) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_bf16(prob(i), prob(i + 1), lsum);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_f16(prob(i), prob(i + 1), lsum);
-    }
-  };
-  if (mode == kModeProxy) {
-    auto keyw = [&](int i) { return wts[32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3)]; };
+template <int MODE, bool BF16>
+__device__ inline void half_probs(const f32x16& sk, int kb, int nv, const float* wts, float c,
+                                  float nmc, int hh, float& lsum, unsigned (&pk)[8]) {
+  if (MODE == kModeProxy) {
+    auto keyw = [&](int i) { return wts[key_of(kb, i, hh)]; };
     auto prob = [&](int i) {
       const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
       return keyw(i) > 0.0f ? e : 0.0f;
     };
-    if (bf16) {
+    if (BF16) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const unsigned a = bf16_rne_bits(prob(i)), b = bf16_rne_bits(prob(i + 1));
@@ -297,50 +293,177 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int mode, int nv, co
         pk[i / 2] = __builtin_bit_cast(unsigned, h);
       }
     }
-  } else if (mode == kModePartial) {
-    emit([&](int i) {
-      const int key = 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-      const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
-      return key < nv ? e : 0.0f;
-    });
+    return;
+  }
+  auto prob = [&](int i) {
+    const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
+    return (MODE == kModePad && key_of(kb, i, hh) >= nv) ? 0.0f : e;
+  };
+  if (BF16) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_bf16(prob(i), prob(i + 1), lsum);
   } else {
-    emit([&](int i) { return __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc)); });
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_f16(prob(i), prob(i + 1), lsum);
   }
 }
 
 // O^T (128 d x 32 queries) += V^T . P^T for one 32-key half kb: 16-key steps
 // ks = 2kb, 2kb+1 with B operand pk[4(ks%2)..+3] (keys 16ks + 8(j/4) + 4hh + j%4);
 // the A operand is row d = 32db + ln of the packed V tile, chunk 2(ks%2) + hh.
-__device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8], bool bf16,
-                               int ln, int hh, f32x16& o0, f32x16& o1, f32x16& o2, f32x16& o3) {
+template <bool BF16>
+__device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8], int ln,
+                               int hh, State& st) {
   const int sw = ((ln >> 1) ^ (ln >> 3)) & 3;
-  if (bf16) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const unsigned char* vb = sv + kb * 8192 + ln * 64 + (((k2 * 2 + hh) ^ sw) << 4);
-      const bf16x8 bb = __builtin_bit_cast(bf16x8, (u32x4){pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]});
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 0 * 2048), bb, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 1 * 2048), bb, o1, 0, 0, 0);
-      o2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 2 * 2048), bb, o2, 0, 0, 0);
-      o3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 3 * 2048), bb, o3, 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const unsigned char* vb = sv + kb * 8192 + ln * 64 + (((k2 * 2 + hh) ^ sw) << 4);
-      const f16x8 bb = __builtin_bit_cast(f16x8, (u32x4){pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]});
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 2048), bb, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 2048), bb, o1, 0, 0, 0);
-      o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 2048), bb, o2, 0, 0, 0);
-      o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 2048), bb, o3, 0, 0, 0);
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const unsigned char* vb = sv + kb * 8192 + ln * 64 + (((k2 * 2 + hh) ^ sw) << 4);
+    const u32x4 pb = {pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
+    if (BF16) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, pb);
+      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 0 * 2048), bb, st.o0, 0, 0, 0);
+      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 1 * 2048), bb, st.o1, 0, 0, 0);
+      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 2 * 2048), bb, st.o2, 0, 0, 0);
+      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 3 * 2048), bb, st.o3, 0, 0, 0);
+    } else {
+      const f16x8 bb = __builtin_bit_cast(f16x8, pb);
+      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 2048), bb, st.o0, 0, 0, 0);
+      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 2048), bb, st.o1, 0, 0, 0);
+      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 2048), bb, st.o2, 0, 0, 0);
+      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 2048), bb, st.o3, 0, 0, 0);
     }
   }
+}
+
+// Everything a tile step needs besides the running state.
+struct Ctx {
+  const AttnParams* p;
+  unsigned char* sk;
+  unsigned char* sv;
+  const float* off;        // proxy logit offsets (log2 weight or -inf), per video block
+  const float* wt;         // proxy denominator weights (0 = no key), per video block
+  int b, h;
+  int64_t bh_tiles;        // (b * heads + h) * nblk
+  int64_t bh_proxy;        // (b * heads + h) * nproxy
+  uint32_t row_bytes, klane, vlane;
+  int w, lane, ln, hh;
+  float c;
+};
+
+template <bool kProxy>
+__device__ inline void issue_tile_k(const Ctx& x, int e) {
+  const AttnParams& p = *x.p;
+  const uint16_t* base;
+  int rmax = kBlock - 1;
+  if (kProxy && (e & kEntProxy)) {
+    const int t = ent_id(e);
+    rmax = min(kBlock - 1, p.nvideo - 1 - kBlock * t);
+    base = p.kmean + (((int64_t)x.b * p.nblk + p.nprefix + (int64_t)kBlock * t) * p.heads + x.h) *
+                         kHeadDim;
+  } else {
+    base = p.k + (((int64_t)x.b * p.seq + (int64_t)ent_id(e) * kBlock) * p.heads + x.h) * kHeadDim;
+  }
+  if (ent_half(e)) issue_k<4, kProxy>(base, x.row_bytes, rmax, 16 * x.w, x.klane, x.lane, x.sk);
+  else issue_k<8, kProxy>(base, x.row_bytes, rmax, 32 * x.w, x.klane, x.lane, x.sk);
+}
+
+template <bool kProxy>
+__device__ inline void issue_tile_v(const Ctx& x, int e) {
+  const AttnParams& p = *x.p;
+  const uint8_t* base = (kProxy && (e & kEntProxy))
+                            ? p.pt + (x.bh_proxy + ent_id(e)) * kTileBytes
+                            : p.vt + (x.bh_tiles + ent_id(e)) * kTileBytes;
+  if (ent_half(e)) issue_v<4>(base, 4096 * x.w, x.vlane, x.sv);
+  else issue_v<8>(base, 8192 * x.w, x.vlane, x.sv);
+}
+
+// One tile: wait for its K rows, S = K Q^T, release K and prefetch the next
+// tile's K rows, running max, wait for its V, probabilities and O += P V,
+// release V and prefetch the next tile's V.  NKB / MODE / BF16 are fixed per
+// tile kind (MODE kModeAny: bf16 tiles, exact or proxy, decided per tile).
+template <bool kProxy, bool kCompute, int NKB, int MODE, bool BF16>
+__device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st, int e, int en,
+                                 bool has_next) {
+  // K(j) has landed once only V(j)'s copies (4 or 8 instructions per wave) are
+  // still in flight.
+  if (NKB == 1) wait_vmcnt<4>(); else wait_vmcnt<8>();
+  wg_barrier();
+  f32x16 s[2];
+  if (kCompute) s_tile<NKB>(x.sk, qop, x.ln, x.hh, s);
+  wg_barrier();   // both waves are done with sK
+  if (has_next) issue_tile_k<kProxy>(x, en);
+
+  const int nv = ent_nv(e);
+  const bool px = kProxy && (MODE == kModeProxy || (MODE == kModeAny && (e & kEntProxy)));
+  const float* offs = kProxy ? x.off + kBlock * ent_id(e) : nullptr;
+  const float* wts = kProxy ? x.wt + kBlock * ent_id(e) : nullptr;
+  if (kCompute) {
+    if (MODE == kModeAny) {
+      if (px) tile_max<NKB, kModeProxy>(s, nv, offs, x.c, x.hh, st);
+      else tile_max<NKB, kModePad>(s, nv, offs, x.c, x.hh, st);
+    } else {
+      tile_max<NKB, MODE>(s, nv, offs, x.c, x.hh, st);
+    }
+  }
+
+  // V(j) has landed once only K(j+1)'s copies may still be in flight.
+  if (has_next) {
+    if (ent_half(en)) wait_vmcnt<4>(); else wait_vmcnt<8>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  wg_barrier();
+  if (kCompute) {
+    const float nmc = -st.mc;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      unsigned pk[8];
+      if (MODE == kModeAny) {
+        if (px) half_probs<kModeProxy, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
+        else half_probs<kModePad, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
+      } else {
+        half_probs<MODE, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
+      }
+      pv_half<BF16>(x.sv, kb, pk, x.ln, x.hh, st);
+    }
+  }
+  wg_barrier();   // both waves are done with sV
+  if (has_next) issue_tile_v<kProxy>(x, en);
+}
+
+// All tiles of one item, kind by kind, in the order of `ord`; gbeg[g] is the
+// first position of kind g (gbeg[kGroups] = number of tiles).
+template <bool kProxy, bool kCompute>
+__device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st, const int* ord,
+                                 const int (&gbeg)[kGroups + 1]) {
+  const int n = gbeg[kGroups];
+  if (n == 0) return;
+  const int e0 = __builtin_amdgcn_readfirstlane(ord[0]);
+  issue_tile_k<kProxy>(x, e0);
+  issue_tile_v<kProxy>(x, e0);
+  auto group = [&](auto body, int g) {
+    const int end = gbeg[g + 1];
+    for (int j = gbeg[g]; j < end; ++j) {
+      const int e = __builtin_amdgcn_readfirstlane(ord[j]);
+      const bool has_next = j + 1 < n;
+      const int en = has_next ? __builtin_amdgcn_readfirstlane(ord[j + 1]) : 0;
+      body(e, en, has_next);
+    }
+  };
+  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, kGFull);
+  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModePad, false>(x, qop, st, e, en, hn); }, kGFullPad);
+  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModeFull, false>(x, qop, st, e, en, hn); }, kGHalf);
+  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModePad, false>(x, qop, st, e, en, hn); }, kGHalfPad);
+  if (kProxy)
+    group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeProxy, false>(x, qop, st, e, en, hn); }, kGProxy);
+  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeAny, true>(x, qop, st, e, en, hn); }, kGBf16);
 }
 
 template <bool kProxy>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
+  __shared__ int sGrp[2 * (kGroups + 1)];   // tiles per kind, then first position per kind
   extern __shared__ int sDyn[];
 
   const int tid = threadIdx.x;
@@ -360,9 +483,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int b = bh / p.heads;
   const int vq = min(max(p.vbs[qb], 0), kBlock);
   const int64_t row_stride = (int64_t)p.heads * kHeadDim;
-  const uint32_t row_bytes = (uint32_t)(row_stride * 2);
-  const uint32_t klane = (uint32_t)(lane >> 4) * row_bytes + (uint32_t)((((lane & 15) ^ (lane >> 4))) << 4);
-  const uint32_t vlane = (uint32_t)lane * 16u;
   uint16_t* out_rows = p.out + (((int64_t)b * p.seq + (int64_t)qb * kBlock) * p.heads + h) * kHeadDim;
 
   if (vq == 0) {   // no valid query row: the whole block is padding
@@ -374,125 +494,127 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   // ---------------- tile table ------------------------------------------
-  Smem sm;
-  sm.k = sK;
-  sm.v = sV;
-  sm.tab = sDyn;
-  sm.cnt = sm.tab + p.table_cap;
-  sm.key = sm.cnt + 4;
-  const int key_cap = kProxy ? (p.nprefix + p.idx_width) : p.idx_width;
-  sm.off = (float*)(sm.key + ((key_cap + 3) & ~3));
-  sm.wt = sm.off + (kProxy ? p.nproxy * kBlock : 0);
-  sm.bits = (unsigned*)(sm.wt + (kProxy ? p.nproxy * kBlock : 0));
-
-  const int64_t bh_tiles = (int64_t)bh * p.nblk;
+  // Candidates: plain items -> the index row; proxy prefix items -> every
+  // block; proxy video items -> prefix blocks, the index row, then the proxy
+  // tiles.  Each valid candidate becomes an entry; entries are ranked by
+  // (kind, block) and then rotated within each exact fp16 kind (see below).
   const bool prefix_item = kProxy && qb < p.nprefix;
-  int nexact;
-  if (prefix_item) {
-    // every block with valid rows, in order (wave 0 compacts with ballots)
-    if (w == 0) {
-      int base = 0;
-      for (int c0 = 0; c0 < p.nblk; c0 += 64) {
-        const int c = c0 + lane;
-        const int nv = c < p.nblk ? min(max(p.vbs[c], 0), kBlock) : 0;
-        const unsigned long long m = __ballot(nv > 0);
-        if (nv > 0) {
-          const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-          sm.tab[pos] = c | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + c] ? kEntBf16 : 0);
-        }
-        base += __popcll(m);
-      }
-      if (lane == 0) sm.cnt[0] = base;
+  const bool video_item = kProxy && !prefix_item;
+  const int ncand = !kProxy ? p.idx_width
+                            : (prefix_item ? p.nblk : p.nprefix + p.idx_width + p.nproxy);
+  int* tab = sDyn;                       // [table_cap] entries
+  int* ord = tab + p.table_cap;          // [table_cap] entries, processing order
+  int* key = ord + p.table_cap;          // [table_cap] sort keys
+  float* off = (float*)(key + p.table_cap);
+  float* wt = off + (kProxy ? p.nproxy * kBlock : 0);
+  unsigned* bits = (unsigned*)(wt + (kProxy ? p.nproxy * kBlock : 0));
+  const int64_t bh_tiles = (int64_t)bh * p.nblk;
+  const int32_t* row = p.idx + (kProxy ? ((int64_t)bh * p.nvideo + (qb - p.nprefix)) * p.idx_width
+                                       : (int64_t)item * p.idx_width);
+  auto candidate = [&](int t) -> int {   // entry of candidate t, or -1
+    int blk;
+    if (!kProxy) {
+      blk = row[t];
+    } else if (prefix_item || t < p.nprefix) {
+      blk = t;
+    } else if (t < p.nprefix + p.idx_width) {
+      const int s = row[t - p.nprefix];
+      blk = (s >= 0 && s < p.nvideo) ? p.nprefix + s : -1;
+    } else {
+      const int pt = t - p.nprefix - p.idx_width;
+      const int rows = min(p.nvideo - kBlock * pt, kBlock);
+      return pt | (rows << kEntNvShift) | kEntProxy |
+             (p.pt_flags[(int64_t)bh * p.nproxy + pt] ? kEntBf16 : 0);
     }
-    wg_barrier();
-    nexact = sm.cnt[0];
-  } else {
-    // selected blocks, sorted ascending (the result does not depend on the
-    // order; a fixed order makes it reproducible bit for bit)
-    const int32_t* row = p.idx + (int64_t)((int64_t)bh * (kProxy ? p.nvideo : p.nblk) +
-                                           (qb - (kProxy ? p.nprefix : 0))) * p.idx_width;
-    for (int t = tid; t < key_cap; t += kThreads) {
-      int blk;
-      if (kProxy) {
-        if (t < p.nprefix) blk = t;
-        else {
-          const int s = row[t - p.nprefix];
-          blk = (s >= 0 && s < p.nvideo) ? p.nprefix + s : -1;
-        }
-      } else {
-        blk = row[t];
-      }
-      const int nv = (blk >= 0 && blk < p.nblk) ? min(max(p.vbs[blk], 0), kBlock) : 0;
-      sm.key[t] = nv > 0 ? blk : 0x7FFFFFFF;
-    }
-    if (tid == 0) sm.cnt[0] = 0;
-    wg_barrier();
-    for (int t = tid; t < key_cap; t += kThreads) {
-      const int key = sm.key[t];
-      if (key != 0x7FFFFFFF) {
-        int rank = 0;
-        for (int u = 0; u < key_cap; ++u) {
-          const int ku = sm.key[u];
-          rank += (ku < key) | ((ku == key) & (u < t));
-        }
-        const int nv = min(max(p.vbs[key], 0), kBlock);
-        sm.tab[rank] = key | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + key] ? kEntBf16 : 0);
-        atomicAdd(&sm.cnt[0], 1);
-      }
-    }
-    wg_barrier();
-    nexact = sm.cnt[0];
+    const int nv = (blk >= 0 && blk < p.nblk) ? min(max(p.vbs[blk], 0), kBlock) : 0;
+    if (nv == 0) return -1;
+    return blk | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + blk] ? kEntBf16 : 0);
+  };
+  if (tid < 2 * (kGroups + 1)) sGrp[tid] = 0;
+  for (int t = tid; t < ncand; t += kThreads) {
+    const int e = candidate(t);
+    key[t] = e < 0 ? 0x7FFFFFFF : (ent_group(e) << 21) | ent_id(e);
+    tab[t] = e;
   }
-  // Phase-aligned sweep: the exact tiles are processed in ascending block order
-  // starting at block `start` and wrapping around.  Workgroups run on an XCD in
-  // dispatch-slot order and take about the same time, so giving slot n the start
-  // n * nblk / phase_slots (phase_slots = workgroups resident per XCD) keeps all
-  // resident workgroups of a head near the same blocks at the same moment: the
-  // XCD's L2 then serves a narrow window of that head's K/V instead of all of it.
-  // The order does not change the result beyond rounding.
-  int rot = 0;
-  {
-    const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.phase_slots) % p.nblk);
-    for (int c0 = 0; c0 < nexact; c0 += 64) {
-      const int t = c0 + lane;
-      const bool before = t < nexact && ent_id(sm.tab[t]) < start;
-      rot += __popcll(__ballot(before));
+  wg_barrier();
+  // rank sort by key, ties by candidate index
+  for (int t = tid; t < ncand; t += kThreads) {
+    const int kt = key[t];
+    if (kt == 0x7FFFFFFF) continue;
+    int rank = 0;
+    for (int u = 0; u < ncand; ++u) {
+      const int ku = key[u];
+      rank += (ku < kt) | ((ku == kt) & (u < t));
     }
+    ord[rank] = tab[t];
+    atomicAdd(&sGrp[ent_group(tab[t])], 1);
   }
-  int ntiles = nexact;
-  if (kProxy && !prefix_item) {
-    // proxy tiles; per proxy key (one per video block) the denominator weight
-    // vbs (0 for selected, empty or out-of-range blocks) and its log2, which
-    // enters the running maximum so that the weighted terms cannot overflow
+  wg_barrier();
+  if (tid == 0) {
+    int acc = 0;
+    for (int g = 0; g < kGroups; ++g) {
+      sGrp[kGroups + 1 + g] = acc;
+      acc += sGrp[g];
+    }
+    sGrp[2 * kGroups + 1] = acc;
+  }
+  wg_barrier();
+  int gbeg[kGroups + 1];
+#pragma unroll
+  for (int g = 0; g <= kGroups; ++g) gbeg[g] = __builtin_amdgcn_readfirstlane(sGrp[kGroups + 1 + g]);
+  const int n = gbeg[kGroups];
+  // Phase-aligned sweep: the exact fp16 tiles of each kind are processed in
+  // ascending block order starting at block `start` and wrapping around.
+  // Workgroups run on an XCD in dispatch-slot order and take about the same
+  // time, so giving slot n the start n * nblk / phase_slots (phase_slots =
+  // workgroups resident per XCD) keeps the resident workgroups of a head near
+  // the same blocks at the same moment: the XCD's L2 then serves a narrow window
+  // of that head's K/V instead of all of it.  The order changes the result only
+  // by rounding.
+  const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.phase_slots) % p.nblk);
+  for (int t = tid; t < n; t += kThreads) tab[t] = ord[t];
+  wg_barrier();
+  for (int t = tid; t < n; t += kThreads) {
+    const int e = tab[t];
+    const int g = ent_group(e);
+    int dst = t;
+    if (g <= kGHalfPad) {
+      const int beg = sGrp[kGroups + 1 + g], cnt = sGrp[g];
+      int lo = beg, hi = beg + cnt;   // first entry of the kind with block >= start
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ent_id(tab[mid]) < start) lo = mid + 1; else hi = mid;
+      }
+      dst = beg + (t - lo + cnt) % cnt;
+    }
+    ord[dst] = e;
+  }
+  if (video_item) {
+    // proxy denominator weights vbs (0 for selected, empty or out-of-range
+    // blocks) and their log2, which enters the running maximum so that the
+    // weighted terms cannot overflow
     const int nbits = (p.nproxy * kBlock) / 32;
-    for (int t = tid; t < nbits; t += kThreads) sm.bits[t] = 0u;
-    for (int t = tid; t < p.nproxy; t += kThreads) {
-      const int rows = min(p.nvideo - kBlock * t, kBlock);
-      sm.tab[nexact + t] = t | (rows << kEntNvShift) | kEntProxy |
-                           (p.pt_flags[(int64_t)bh * p.nproxy + t] ? kEntBf16 : 0);
-    }
+    for (int t = tid; t < nbits; t += kThreads) bits[t] = 0u;
     wg_barrier();
-    const int32_t* row = p.idx + ((int64_t)bh * p.nvideo + (qb - p.nprefix)) * p.idx_width;
     for (int t = tid; t < p.idx_width; t += kThreads) {
       const int s = row[t];
-      if (s >= 0 && s < p.nvideo) atomicOr(&sm.bits[s >> 5], 1u << (s & 31));
+      if (s >= 0 && s < p.nvideo) atomicOr(&bits[s >> 5], 1u << (s & 31));
     }
     wg_barrier();
     for (int vblk = tid; vblk < p.nproxy * kBlock; vblk += kThreads) {
       float o = -INFINITY, wv = 0.0f;
       if (vblk < p.nvideo) {
         const int nv = min(max(p.vbs[p.nprefix + vblk], 0), kBlock);
-        if (nv > 0 && !((sm.bits[vblk >> 5] >> (vblk & 31)) & 1u)) {
+        if (nv > 0 && !((bits[vblk >> 5] >> (vblk & 31)) & 1u)) {
           o = __log2f((float)nv);
           wv = (float)nv;
         }
       }
-      sm.off[vblk] = o;
-      sm.wt[vblk] = wv;
+      off[vblk] = o;
+      wt[vblk] = wv;
     }
-    ntiles += p.nproxy;
-    wg_barrier();
   }
+  wg_barrier();
 
   // ---------------- per-wave state ---------------------------------------
   const bool active = 32 * w < vq;      // wave has at least one valid query row
@@ -504,116 +626,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool qvalid = qrow < vq;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qvalid) x = *(const u32x4*)(qp + 16 * s);
-      qop[s] = __builtin_bit_cast(bf16x8, x);
+      u32x4 v4 = {0u, 0u, 0u, 0u};
+      if (qvalid) v4 = *(const u32x4*)(qp + 16 * s);
+      qop[s] = __builtin_bit_cast(bf16x8, v4);
     }
   }
   // Let the Q loads finish here, so that inside the loop the only outstanding
-  // vector-memory operations are the tile copies counted by wait_vmcnt_rt.
+  // vector-memory operations are the tile copies counted by wait_vmcnt.
   wait_vmcnt<0>();
-  f32x16 o0 = {}, o1 = {}, o2 = {}, o3 = {};
-  float mc = -INFINITY;   // running max of the scaled logits (log2 units)
-  float lsum = 0.0f;      // this lane's share of the softmax denominator
-  const float c = p.c;
 
-  auto k_src = [&](int e, int& rmax) -> const uint16_t* {
-    if (kProxy && (e & kEntProxy)) {
-      const int t = ent_id(e);
-      rmax = min(kBlock - 1, p.nvideo - 1 - kBlock * t);
-      return p.kmean + (((int64_t)b * p.nblk + p.nprefix + (int64_t)kBlock * t) * p.heads + h) *
-                           kHeadDim;
-    }
-    rmax = kBlock - 1;
-    return p.k + (((int64_t)b * p.seq + (int64_t)ent_id(e) * kBlock) * p.heads + h) * kHeadDim;
-  };
-  auto v_src = [&](int e) -> const uint8_t* {
-    if (kProxy && (e & kEntProxy))
-      return p.pt + ((int64_t)bh * p.nproxy + ent_id(e)) * kTileBytes;
-    return p.vt + (bh_tiles + ent_id(e)) * kTileBytes;
-  };
-  auto issue_tile_k = [&](int e) {
-    int rmax;
-    const uint16_t* ks = k_src(e, rmax);
-    if (ent_nv(e) <= 32) issue_k<4, kProxy>(ks, row_bytes, rmax, 16 * w, klane, lane, sK);
-    else issue_k<8, kProxy>(ks, row_bytes, rmax, 32 * w, klane, lane, sK);
-  };
-  auto issue_tile_v = [&](int e) {
-    if (ent_nv(e) <= 32) issue_v<4>(v_src(e), 4096 * w, vlane, sV);
-    else issue_v<8>(v_src(e), 8192 * w, vlane, sV);
-  };
-
-  auto tab_at = [&](int j) -> int {
-    int jj = j;
-    if (j < nexact) {
-      jj = j + rot;
-      if (jj >= nexact) jj -= nexact;
-    }
-    return __builtin_amdgcn_readfirstlane(sm.tab[jj]);
-  };
-
-  if (ntiles > 0) {
-    const int e0 = tab_at(0);
-    issue_tile_k(e0);
-    issue_tile_v(e0);
-  }
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int e = tab_at(j);
-    const int en = (j + 1 < ntiles) ? tab_at(j + 1) : 0;
-    const int nv = ent_nv(e);
-    const bool half = nv <= 32;
-    const int mode = (kProxy && (e & kEntProxy)) ? kModeProxy : ((nv & 31) ? kModePartial : kModeFull);
-    const bool is_bf16 = (e & kEntBf16) != 0;
-
-    // K(j) has landed once only V(j)'s copies may still be in flight.
-    if (half) wait_vmcnt<4>(); else wait_vmcnt<8>();
-    wg_barrier();
-    f32x16 s[2];
-    if (active) {
-      if (half) s_tile<1>(sK, qop, ln, hh, s);
-      else s_tile<2>(sK, qop, ln, hh, s);
-    }
-    wg_barrier();   // both waves are done with sK
-    if (j + 1 < ntiles) issue_tile_k(en);
-
-    bool live = false;
-    const float* offs = kProxy ? sm.off + kBlock * ent_id(e) : nullptr;
-    const float* wts = kProxy ? sm.wt + kBlock * ent_id(e) : nullptr;
-    if (active) {
-      if (half) live = tile_max<1>(s, mode, nv, offs, c, hh, mc, lsum, o0, o1, o2, o3);
-      else live = tile_max<2>(s, mode, nv, offs, c, hh, mc, lsum, o0, o1, o2, o3);
-    }
-
-    // V(j) has landed once only K(j+1)'s copies may still be in flight.
-    if (j + 1 < ntiles) {
-      if (ent_nv(en) <= 32) wait_vmcnt<4>(); else wait_vmcnt<8>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    wg_barrier();
-    if (live) {
-      const float nmc = -mc;
-      {
-        unsigned pk[8];
-        half_probs(s[0], 0, mode, nv, offs, wts, is_bf16, c, nmc, hh, lsum, pk);
-        pv_half(sV, 0, pk, is_bf16, ln, hh, o0, o1, o2, o3);
-      }
-      if (!half) {
-        unsigned pk[8];
-        half_probs(s[1], 1, mode, nv, offs, wts, is_bf16, c, nmc, hh, lsum, pk);
-        pv_half(sV, 1, pk, is_bf16, ln, hh, o0, o1, o2, o3);
-      }
-    }
-    wg_barrier();   // both waves are done with sV
-    if (j + 1 < ntiles) issue_tile_v(en);
+  Ctx x;
+  x.p = &p;
+  x.sk = sK;
+  x.sv = sV;
+  x.off = off;
+  x.wt = wt;
+  x.b = b;
+  x.h = h;
+  x.bh_tiles = bh_tiles;
+  x.bh_proxy = (int64_t)bh * p.nproxy;
+  x.row_bytes = (uint32_t)(row_stride * 2);
+  x.klane = (uint32_t)(lane >> 4) * x.row_bytes + (uint32_t)((((lane & 15) ^ (lane >> 4))) << 4);
+  x.vlane = (uint32_t)lane * 16u;
+  x.w = w;
+  x.lane = lane;
+  x.ln = ln;
+  x.hh = hh;
+  x.c = p.c;
+  State st;
+  st.o0 = f32x16{};
+  st.o1 = f32x16{};
+  st.o2 = f32x16{};
+  st.o3 = f32x16{};
+  st.mc = -INFINITY;
+  st.lsum = 0.0f;
+  if (n > 0) {
+    if (active) run_tiles<kProxy, true>(x, qop, st, ord, gbeg);
+    else run_tiles<kProxy, false>(x, qop, st, ord, gbeg);
   }
 
   // ---------------- epilogue ---------------------------------------------
   // o = O / l for valid rows; padding rows, empty rows and non-finite results
   // are written as 0.  Lane (ln, hh) holds query row 32w+ln and, in register
   // 4a+r of accumulator db, head-dim index 32db + 8a + 4hh + r.
-  const float l_tot = pair_sum(lsum);
+  const float l_tot = pair_sum(st.lsum);
   const bool row_ok = active && qrow < vq && l_tot > 0.0f;
   const float inv = row_ok ? 1.0f / l_tot : 0.0f;
   uint16_t* orow = out_rows + (int64_t)qrow * row_stride + 4 * hh;
@@ -623,26 +679,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       unsigned u[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = acc[4 * a + r] * inv;
-        if (!row_ok || !isfinite(x)) x = 0.0f;
-        u[r] = bf16_rne_bits(x);
+        float v = acc[4 * a + r] * inv;
+        if (!row_ok || !isfinite(v)) v = 0.0f;
+        u[r] = bf16_rne_bits(v);
       }
       *(u32x2*)(orow + 32 * db + 8 * a) = (u32x2){u[0] | (u[1] << 16), u[2] | (u[3] << 16)};
     }
   };
-  store4(o0, 0);
-  store4(o1, 1);
-  store4(o2, 2);
-  store4(o3, 3);
+  store4(st.o0, 0);
+  store4(st.o1, 1);
+  store4(st.o2, 2);
+  store4(st.o3, 3);
 }
 
 }  // namespace
 
+size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
+  size_t dyn = (size_t)p.table_cap * 4 * 3;
+  if (proxy) dyn += (size_t)p.nproxy * kBlock * 8 + (size_t)p.nproxy * 2 * 4;
+  return dyn;
+}
+
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream) {
   if (p.n_items <= 0) return hipSuccess;
-  const int key_cap = proxy ? (p.nprefix + p.idx_width) : p.idx_width;
-  size_t dyn = (size_t)p.table_cap * 4 + 16 + (size_t)((key_cap + 3) & ~3) * 4;
-  if (proxy) dyn += (size_t)p.nproxy * kBlock * 8 + (size_t)p.nproxy * 2 * 4;
+  const size_t dyn = attn_dyn_lds(p, proxy);
   const unsigned grid = (unsigned)p.items_per_xcd * 8u;
   if (proxy)
     hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, p);

@@ -59,5 +59,7 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+// Dynamic LDS bytes launch_attn requests for these parameters.
+size_t attn_dyn_lds(const AttnParams& p, bool proxy);
 
 }  // namespace vsa
