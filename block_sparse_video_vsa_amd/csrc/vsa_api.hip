@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 using namespace vsa;
 
 namespace {
@@ -12,6 +14,8 @@ namespace {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
 constexpr int64_t kMaxBlocks = (1 << 20) - 1;
+
+std::atomic<int> g_deterministic{0};
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -51,10 +55,8 @@ AttnParams base_params(int32_t batch, int32_t seq_len, int32_t num_heads, float 
   p.nblk = seq_len / kBlock;
   p.n_items = batch * num_heads * p.nblk;
   p.items_per_xcd = (p.n_items + 7) / 8;
-  // 32 CUs per XCD x 4 resident workgroups per CU (two wave64s each, 256 VGPRs,
-  // about 33 KB of LDS)
-  p.phase_slots = 128;
   p.c = sm_scale * 1.4426950408889634f;   // log2(e): softmax evaluated with exp2
+  p.deterministic = g_deterministic.load(std::memory_order_relaxed);
   return p;
 }
 
@@ -72,6 +74,14 @@ extern "C" const char* vsa_status_string(vsa_status s) {
     case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale must be finite and >= 0";
   }
   return "VSA_ERR_UNKNOWN";
+}
+
+extern "C" void vsa_set_deterministic(int32_t enable) {
+  g_deterministic.store(enable ? 1 : 0, std::memory_order_relaxed);
+}
+
+extern "C" int32_t vsa_get_deterministic(void) {
+  return g_deterministic.load(std::memory_order_relaxed);
 }
 
 extern "C" size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,

@@ -30,13 +30,25 @@
 // the LDS layout, so their copy is linear.  Tiles whose vbs is <= 32 load and
 // multiply only their first 32 keys.
 //
-// Tiles are processed grouped by kind (full, full with padding keys, half, half
-// with padding keys, proxy, bf16), each kind by a straight-line specialisation
-// of the tile step, so the accumulators never cross data-dependent control flow
-// except the rescale.
+// Tile order (it changes results only by rounding): the exact fp16 tiles of an
+// item are swept in ascending block order from a start block, in nseg segments
+// of the block range; inside a segment they go kind by kind (full, full with
+// padding keys, half, half with padding keys), each kind through a straight-line
+// specialisation of the tile step, so the accumulators never cross
+// data-dependent control flow except the rescale.  Proxy and bf16 tiles follow.
+// The start block is the average sweep position of the workgroups running on
+// the same XCD (a per-XCD progress counter that every workgroup advances after
+// each segment), so the resident workgroups of a head move through its blocks
+// together and the XCD's L2 holds a narrow window of that head's K/V tiles
+// instead of all of them.  In deterministic mode the start depends only on the
+// workgroup index, so the order, and with it the rounding, is reproducible.
 #include "vsa_internal.h"
 
 #include <math.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace vsa {
 namespace {
@@ -77,6 +89,15 @@ __device__ inline int ent_group(int e) {
   if (nv == 32) return kGHalf;
   return kGHalfPad;
 }
+
+// Sweep progress per XCD, in blocks swept by all workgroups of all launches
+// (wraps modulo 2^64).  Divided by the number of resident workgroups it is a
+// virtual clock that advances at their average sweep rate; a starting workgroup
+// begins its sweep at that position.  Only the tile order depends on it.  The
+// counter of XCD x is touched only by workgroups running there, which share
+// that XCD's L2, so workgroup-scope atomics and loads (served by the L2) are
+// enough; device scope would send every access past the L2.
+__device__ unsigned long long g_sweep_progress[8];
 
 // Softmax variants of a tile step.
 enum : int { kModeFull = 0, kModePad = 1, kModeProxy = 2, kModeAny = 3 };
@@ -346,7 +367,7 @@ struct Ctx {
   int64_t bh_tiles;        // (b * heads + h) * nblk
   int64_t bh_proxy;        // (b * heads + h) * nproxy
   uint32_t row_bytes, klane, vlane;
-  int w, lane, ln, hh;
+  int w, lane, ln, hh, tid, xcd;
   float c;
 };
 
@@ -431,39 +452,52 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   if (has_next) issue_tile_v<kProxy>(x, en);
 }
 
-// All tiles of one item, kind by kind, in the order of `ord`; gbeg[g] is the
-// first position of kind g (gbeg[kGroups] = number of tiles).
+// Table cells: segment s, exact fp16 kind g -> 4 s + g; then proxy, bf16.
+__device__ inline int cell_proxy(int nseg) { return 4 * nseg; }
+__device__ inline int cell_bf16(int nseg) { return 4 * nseg + 1; }
+__device__ inline int seg_first(int s, int nblk, int nseg) { return (s * nblk + nseg - 1) / nseg; }
+
+// All tiles of one item in the order of `ord`; cbeg[c] is the first position of
+// cell c (cbeg[4 nseg + 2] = number of tiles).  As each segment begins, the
+// sweep progress counter of the XCD advances by the segment's width in blocks.
 template <bool kProxy, bool kCompute>
 __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st, const int* ord,
-                                 const int (&gbeg)[kGroups + 1]) {
-  const int n = gbeg[kGroups];
-  if (n == 0) return;
+                                 const int* cbeg, int nseg, int n) {
   const int e0 = __builtin_amdgcn_readfirstlane(ord[0]);
   issue_tile_k<kProxy>(x, e0);
   issue_tile_v<kProxy>(x, e0);
-  auto group = [&](auto body, int g) {
-    const int end = gbeg[g + 1];
-    for (int j = gbeg[g]; j < end; ++j) {
+  auto cell = [&](auto body, int c) {
+    const int beg = __builtin_amdgcn_readfirstlane(cbeg[c]);
+    const int end = __builtin_amdgcn_readfirstlane(cbeg[c + 1]);
+    for (int j = beg; j < end; ++j) {
       const int e = __builtin_amdgcn_readfirstlane(ord[j]);
       const bool has_next = j + 1 < n;
       const int en = has_next ? __builtin_amdgcn_readfirstlane(ord[j + 1]) : 0;
       body(e, en, has_next);
     }
   };
-  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, kGFull);
-  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModePad, false>(x, qop, st, e, en, hn); }, kGFullPad);
-  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModeFull, false>(x, qop, st, e, en, hn); }, kGHalf);
-  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModePad, false>(x, qop, st, e, en, hn); }, kGHalfPad);
+  const int nblk = x.p->nblk;
+  for (int s = 0; s < nseg; ++s) {
+    if (x.tid == 0 && !x.p->deterministic)
+      __hip_atomic_fetch_add(&g_sweep_progress[x.xcd],
+                             (unsigned long long)(seg_first(s + 1, nblk, nseg) - seg_first(s, nblk, nseg)),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGFull);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModePad, false>(x, qop, st, e, en, hn); }, 4 * s + kGFullPad);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGHalf);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModePad, false>(x, qop, st, e, en, hn); }, 4 * s + kGHalfPad);
+  }
   if (kProxy)
-    group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeProxy, false>(x, qop, st, e, en, hn); }, kGProxy);
-  group([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeAny, true>(x, qop, st, e, en, hn); }, kGBf16);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeProxy, false>(x, qop, st, e, en, hn); }, cell_proxy(nseg));
+  cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeAny, true>(x, qop, st, e, en, hn); }, cell_bf16(nseg));
 }
 
 template <bool kProxy>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
-  __shared__ int sGrp[2 * (kGroups + 1)];   // tiles per kind, then first position per kind
+  __shared__ int sCell[2 * (4 * kMaxSeg + 2) + 1];   // tiles per cell, then first position per cell
+  __shared__ int sStart;
   extern __shared__ int sDyn[];
 
   const int tid = threadIdx.x;
@@ -475,7 +509,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // XCD-aware item order: consecutive workgroup ids go round-robin to the 8
   // XCDs, so XCD x gets a contiguous run of items (whole heads) and its L2
   // serves one head's K/V at a time.
-  const int item = (int)(blockIdx.x & 7) * p.items_per_xcd + (int)(blockIdx.x >> 3);
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = xcd * p.items_per_xcd + (int)(blockIdx.x >> 3);
   if (item >= p.n_items) return;
   const int qb = item % p.nblk;
   const int bh = item / p.nblk;
@@ -496,8 +531,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---------------- tile table ------------------------------------------
   // Candidates: plain items -> the index row; proxy prefix items -> every
   // block; proxy video items -> prefix blocks, the index row, then the proxy
-  // tiles.  Each valid candidate becomes an entry; entries are ranked by
-  // (kind, block) and then rotated within each exact fp16 kind (see below).
+  // tiles.  Each valid candidate becomes an entry; entries are sorted by
+  // (cell, block position in the sweep).
   const bool prefix_item = kProxy && qb < p.nprefix;
   const bool video_item = kProxy && !prefix_item;
   const int ncand = !kProxy ? p.idx_width
@@ -530,14 +565,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (nv == 0) return -1;
     return blk | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + blk] ? kEntBf16 : 0);
   };
-  if (tid < 2 * (kGroups + 1)) sGrp[tid] = 0;
+  const int nseg = p.nseg;
+  const int ncell = 4 * nseg + 2;
+  int* ccnt = sCell;                     // [ncell] tiles per cell
+  int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
+  if (tid == 0) {
+    if (p.deterministic) {
+      // Start block from the dispatch slot: resident workgroups spread evenly.
+      sStart = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.sweep_slots) % p.nblk);
+    } else {
+      // Start block: the average position of the XCD's resident workgroups.
+      const unsigned long long prog =
+          __hip_atomic_load(&g_sweep_progress[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      sStart = (int)((prog / (unsigned long long)p.sweep_slots) % (unsigned long long)p.nblk);
+    }
+  }
+  for (int t = tid; t < 2 * ncell + 1; t += kThreads) sCell[t] = 0;
+  for (int t = tid; t < ncand; t += kThreads) tab[t] = candidate(t);
+  wg_barrier();
+  const int start = sStart;
   for (int t = tid; t < ncand; t += kThreads) {
-    const int e = candidate(t);
-    key[t] = e < 0 ? 0x7FFFFFFF : (ent_group(e) << 21) | ent_id(e);
-    tab[t] = e;
+    const int e = tab[t];
+    int k = 0x7FFFFFFF;
+    if (e >= 0) {
+      const int g = ent_group(e);
+      if (g <= kGHalfPad) {
+        const int rel = ent_id(e) - start + (ent_id(e) < start ? p.nblk : 0);
+        k = ((4 * (rel * nseg / p.nblk) + g) << 20) | rel;
+      } else {
+        k = ((g == kGProxy ? cell_proxy(nseg) : cell_bf16(nseg)) << 20) | ent_id(e);
+      }
+    }
+    key[t] = k;
   }
   wg_barrier();
-  // rank sort by key, ties by candidate index
+  // rank sort by key, ties (repeated blocks) by candidate index
   for (int t = tid; t < ncand; t += kThreads) {
     const int kt = key[t];
     if (kt == 0x7FFFFFFF) continue;
@@ -547,47 +609,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       rank += (ku < kt) | ((ku == kt) & (u < t));
     }
     ord[rank] = tab[t];
-    atomicAdd(&sGrp[ent_group(tab[t])], 1);
+    atomicAdd(&ccnt[kt >> 20], 1);
   }
   wg_barrier();
   if (tid == 0) {
     int acc = 0;
-    for (int g = 0; g < kGroups; ++g) {
-      sGrp[kGroups + 1 + g] = acc;
-      acc += sGrp[g];
+    for (int c = 0; c < ncell; ++c) {
+      cbeg[c] = acc;
+      acc += ccnt[c];
     }
-    sGrp[2 * kGroups + 1] = acc;
-  }
-  wg_barrier();
-  int gbeg[kGroups + 1];
-#pragma unroll
-  for (int g = 0; g <= kGroups; ++g) gbeg[g] = __builtin_amdgcn_readfirstlane(sGrp[kGroups + 1 + g]);
-  const int n = gbeg[kGroups];
-  // Phase-aligned sweep: the exact fp16 tiles of each kind are processed in
-  // ascending block order starting at block `start` and wrapping around.
-  // Workgroups run on an XCD in dispatch-slot order and take about the same
-  // time, so giving slot n the start n * nblk / phase_slots (phase_slots =
-  // workgroups resident per XCD) keeps the resident workgroups of a head near
-  // the same blocks at the same moment: the XCD's L2 then serves a narrow window
-  // of that head's K/V instead of all of it.  The order changes the result only
-  // by rounding.
-  const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.phase_slots) % p.nblk);
-  for (int t = tid; t < n; t += kThreads) tab[t] = ord[t];
-  wg_barrier();
-  for (int t = tid; t < n; t += kThreads) {
-    const int e = tab[t];
-    const int g = ent_group(e);
-    int dst = t;
-    if (g <= kGHalfPad) {
-      const int beg = sGrp[kGroups + 1 + g], cnt = sGrp[g];
-      int lo = beg, hi = beg + cnt;   // first entry of the kind with block >= start
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (ent_id(tab[mid]) < start) lo = mid + 1; else hi = mid;
-      }
-      dst = beg + (t - lo + cnt) % cnt;
-    }
-    ord[dst] = e;
+    cbeg[ncell] = acc;
   }
   if (video_item) {
     // proxy denominator weights vbs (0 for selected, empty or out-of-range
@@ -617,6 +648,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   wg_barrier();
 
   // ---------------- per-wave state ---------------------------------------
+  const int n = __builtin_amdgcn_readfirstlane(cbeg[ncell]);
   const bool active = 32 * w < vq;      // wave has at least one valid query row
   const int qrow = 32 * w + ln;         // query row inside the block
   bf16x8 qop[8];
@@ -652,6 +684,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   x.lane = lane;
   x.ln = ln;
   x.hh = hh;
+  x.tid = tid;
+  x.xcd = xcd;
   x.c = p.c;
   State st;
   st.o0 = f32x16{};
@@ -661,8 +695,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   st.mc = -INFINITY;
   st.lsum = 0.0f;
   if (n > 0) {
-    if (active) run_tiles<kProxy, true>(x, qop, st, ord, gbeg);
-    else run_tiles<kProxy, false>(x, qop, st, ord, gbeg);
+    if (active) run_tiles<kProxy, true>(x, qop, st, ord, cbeg, nseg, n);
+    else run_tiles<kProxy, false>(x, qop, st, ord, cbeg, nseg, n);
   }
 
   // ---------------- epilogue ---------------------------------------------
@@ -700,9 +734,40 @@ size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
   return dyn;
 }
 
-hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream) {
-  if (p.n_items <= 0) return hipSuccess;
+namespace {
+
+// Attention workgroups resident per XCD at once for this dynamic LDS size,
+// cached per (device, variant, LDS size).
+int resident_per_xcd(bool proxy, size_t dyn) {
+  struct Entry { int dev; bool proxy; size_t dyn; int slots; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.dev == dev && e.proxy == proxy && e.dyn == dyn) return e.slots;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 8;
+  const hipError_t err = proxy
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<true>, kThreads, dyn)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<false>, kThreads, dyn);
+  if (err != hipSuccess) per_cu = 1;
+  const int slots = std::max(1, per_cu * cus / 8);
+  cache.push_back({dev, proxy, dyn, slots});
+  return slots;
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream) {
+  if (params.n_items <= 0) return hipSuccess;
+  AttnParams p = params;
   const size_t dyn = attn_dyn_lds(p, proxy);
+  p.sweep_slots = resident_per_xcd(proxy, dyn);
+  // about ten tiles of a typical item per sweep segment
+  const int tiles = p.idx_width + (proxy ? p.nprefix + p.nproxy : 0);
+  p.nseg = std::min(kMaxSeg, std::max(1, (tiles + 5) / 10));
   const unsigned grid = (unsigned)p.items_per_xcd * 8u;
   if (proxy)
     hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, p);

@@ -10,6 +10,7 @@ namespace vsa {
 constexpr int kBlock = 64;       // tokens per cube / block
 constexpr int kHeadDim = 128;    // head geometry fixed at compile time
 constexpr int kTileBytes = kBlock * kHeadDim * 2;   // one 64 x 128 16-bit tile
+constexpr int kMaxSeg = 16;     // most sweep segments per item
 
 // ---- packed V tiles ------------------------------------------------------
 // Each (batch, head, tile) V^T tile is 16 KB: two 8 KB key halves (keys 0-31,
@@ -50,7 +51,9 @@ struct AttnParams {
   int n_items;              // batch * heads * nblk
   int items_per_xcd;
   int table_cap;            // tile-table capacity (entries)
-  int phase_slots;          // workgroups resident per XCD (sweep phase period)
+  int sweep_slots;          // workgroups resident per XCD at once
+  int nseg;                 // sweep segments per item (1..kMaxSeg)
+  int deterministic;        // 1: sweep start from the workgroup index only
   float c;                  // sm_scale * log2(e)
 };
 

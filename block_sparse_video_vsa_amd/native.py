@@ -8,6 +8,7 @@ call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -32,6 +33,8 @@ _f32 = ctypes.c_float
 # (name, restype, argtypes)
 _SIGNATURES = {
     "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "vsa_set_deterministic": (None, [_i32]),
+    "vsa_get_deterministic": (_i32, []),
     "vsa_fwd_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "vsa_fwd": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t, _c_void_p]),
@@ -77,6 +80,26 @@ def load_library() -> ctypes.CDLL:
 
 def status_string(status: int) -> str:
     return load_library().vsa_status_string(int(status)).decode()
+
+
+def set_deterministic(enable: bool) -> None:
+    """Process-wide accumulation-order switch (vsa_set_deterministic)."""
+    load_library().vsa_set_deterministic(1 if enable else 0)
+
+
+def get_deterministic() -> bool:
+    return bool(load_library().vsa_get_deterministic())
+
+
+@contextlib.contextmanager
+def deterministic(enable: bool = True):
+    """Run the enclosed calls with deterministic mode set to `enable`."""
+    prev = get_deterministic()
+    set_deterministic(enable)
+    try:
+        yield
+    finally:
+        set_deterministic(prev)
 
 
 def _check(fn: str, status: int) -> None:

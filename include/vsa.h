@@ -62,6 +62,19 @@ typedef enum vsa_status {
 const char* vsa_status_string(vsa_status s);
 
 /*
+ * Accumulation order.  The attention kernels visit each query cube's KV tiles
+ * in an order chosen for L2 reuse.  By default that order follows the live
+ * progress of the other workgroups on the same XCD (a per-device counter held
+ * by the library), so two identical calls may differ in the last bits of fp32
+ * rounding, always within the documented accuracy.  With deterministic mode on,
+ * the order depends only on the shapes and the inputs: repeated calls give
+ * bitwise identical outputs, at some speed cost.  The setting is process-wide,
+ * thread-safe, and applies to calls made after it returns.
+ */
+void vsa_set_deterministic(int32_t enable);
+int32_t vsa_get_deterministic(void);
+
+/*
  * Workspace bytes vsa_fwd needs for this shape (0 if the shape is invalid).
  * The workspace holds each (batch, head, cube) V tile transposed to key-major
  * half precision, plus one byte per tile; it is fully rewritten by every call.
@@ -75,8 +88,9 @@ size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
  *   q, k, v       bf16 [batch, seq_len, num_heads, head_dim], cube-major tiled:
  *                 rows 64c .. 64c+63 form cube c.
  *   topk_idx      int32 [batch, num_heads, seq_len/64, topk]: selected KV cubes
- *                 of each (batch, head, query cube); any order (the result does
- *                 not depend on it).
+ *                 of each (batch, head, query cube), in any order (the kernel
+ *                 sorts each row; in deterministic mode the output is bitwise
+ *                 independent of the order).
  *   vbs           int32 [seq_len/64]: valid rows of each cube, shared by all
  *                 batches and heads; rows >= vbs[c] are padding on both the
  *                 query and the key side.

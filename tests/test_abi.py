@@ -29,10 +29,23 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"vsa_fwd", "vsa_preprocess", "vsa_fwd_proxy", "vsa_status_string",
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
-            "vsa_fwd_prepacked"} <= set(names)
+            "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
+
+
+def test_deterministic_switch(lib):
+    assert native.get_deterministic() is False
+    with native.deterministic():
+        assert lib.vsa_get_deterministic() == 1
+        with native.deterministic(False):
+            assert native.get_deterministic() is False
+        assert native.get_deterministic() is True
+    assert lib.vsa_get_deterministic() == 0
+    lib.vsa_set_deterministic(7)          # any non-zero value turns it on
+    assert lib.vsa_get_deterministic() == 1
+    lib.vsa_set_deterministic(0)
 
 
 def test_status_strings(lib):
