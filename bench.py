@@ -35,6 +35,36 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_config2_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_video_vsa_amd", "csrc", f)
+                  for f in ("vsa_attn.hip", "vsa_internal.h")]
+
+
+def measured_traffic(config: str):
+    """HBM-side bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated), or None when that summary is for another
+    workload or was taken on different kernel sources."""
+    if config != "2" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line:
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, n_items: int, seed: int = 0) -> dict:
     """Time the fp64 oracle on a bounded, seeded sample of (b, h, cube) items."""
     from oracle import vsa_oracle as O
@@ -178,7 +208,8 @@ def main():
                        "attention_p50": round(float(np.median(attn_ms)), 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg.name),
+                     "traffic_unit": "bytes per launch, HBM side (copy-calibrated FETCH_SIZE + WRITE_SIZE)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
