@@ -14,6 +14,7 @@ namespace {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
 constexpr int64_t kMaxBlocks = (1 << 20) - 1;
+constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stays below 2^32 bytes
 
 std::atomic<int> g_deterministic{0};
 
@@ -39,7 +40,8 @@ bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 vsa_status check_common(int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim) {
   if (head_dim != kHeadDim) return VSA_ERR_UNSUPPORTED;
-  if (batch < 1 || num_heads < 1 || seq_len < kBlock || seq_len % kBlock != 0)
+  if (batch < 1 || num_heads < 1 || num_heads > kMaxHeads || seq_len < kBlock ||
+      seq_len % kBlock != 0)
     return VSA_ERR_SHAPE;
   const int64_t nblk = seq_len / kBlock;
   if (nblk > kMaxBlocks) return VSA_ERR_SHAPE;

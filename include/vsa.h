@@ -32,6 +32,9 @@
  *   - Calls that share a workspace must not overlap in time.
  *   - Only head_dim == 128 is supported ([SH]; the head geometry is fixed at
  *     compile time, as in [RUN]).
+ *   - Size limits (VSA_ERR_SHAPE otherwise): seq_len a positive multiple of 64
+ *     with at most 2^20 - 1 cubes, 1 <= num_heads <= 65536, batch >= 1, and
+ *     batch * num_heads * seq_len/64 < 2^31.
  */
 #ifndef VSA_H
 #define VSA_H
