@@ -89,6 +89,119 @@ def cpu_baseline(wl, n_items: int, seed: int = 0) -> dict:
                       f"{dt:.1f} s, {flops / 1e9:.1f} effective GFLOP, fp64 numpy"}
 
 
+def cpu_baseline_proxy(wl, km, vs, n_items: int, seed: int = 0) -> dict:
+    """Time the fp64 proxy oracle on a bounded, seeded sample of video query blocks."""
+    from oracle import vsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cfg = wl.config
+    B, S, H, D = wl.q.shape
+    rng = np.random.default_rng(seed)
+    items = [(int(rng.integers(B)), int(rng.integers(H)),
+              int(rng.integers(cfg.n_prefix_blocks, cfg.n_blocks))) for _ in range(n_items)]
+    from block_sparse_video_vsa_amd import workloads as W
+    fe, fp = W.effective_flops_proxy(wl.sel_idx, wl.vbs, cfg.n_prefix_blocks)
+    per_item = (fe + fp) / (B * H * cfg.n_blocks)   # average work per item (prefix items excluded from the sample)
+    t0 = time.perf_counter()
+    for b, h, qb in items:
+        O.vsa_fwd_proxy_item(wl.q, wl.k, wl.v, wl.sel_idx, wl.vbs, km, vs, cfg.prefix_len,
+                             wl.sm_scale, b, h, qb)
+    dt = time.perf_counter() - t0
+    return {"value": float(per_item * n_items / dt / 1e12), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_items} random (batch, head, video query block) items, {dt:.1f} s, "
+                      "work per item taken as the workload average, fp64 numpy; block summaries "
+                      "from the oracle's preprocess, computed before timing"}
+
+
+def bench_proxy(args, cfg, dev):
+    """Packed [prefix | video] proxy-compensated path: vsa_preprocess + vsa_fwd_proxy."""
+    import torch
+
+    import block_sparse_video_vsa_amd as vsa
+    from block_sparse_video_vsa_amd import workloads as W
+
+    t0 = time.perf_counter()
+    wl = W.generate(cfg)
+    log(f"generated config {cfg.name} in {time.perf_counter() - t0:.1f} s")
+    B, S, H, D = wl.q.shape
+    f_exact, f_proxy = W.effective_flops_proxy(wl.sel_idx, wl.vbs, cfg.n_prefix_blocks)
+
+    def up(x, bf16=False):
+        x = np.ascontiguousarray(x)
+        t = torch.from_numpy(x.view(np.int16) if bf16 else x)
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    q, k, v = up(wl.q, True), up(wl.k, True), up(wl.v, True)
+    sel, vbs = up(wl.sel_idx), up(wl.vbs)
+    km = torch.empty((B, S // 64, H, D), dtype=torch.bfloat16, device=dev)
+    vs = torch.empty_like(km)
+    out = torch.empty_like(q)
+    ws = torch.empty(vsa.proxy_workspace_size(B, S, cfg.prefix_len, H), dtype=torch.uint8, device=dev)
+    scale = float(wl.sm_scale)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vsa.vsa_preprocess(k, v, vbs, km, vs)
+        if ev is not None:
+            ev[1].record(stream)
+        vsa.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, cfg.prefix_len, scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    # preprocess moves the valid K and V rows in and the two summaries out
+    n_valid = int(np.minimum(np.maximum(wl.vbs, 0), 64).sum())
+    pre_bytes = 2.0 * B * n_valid * H * D * 2 + 2.0 * B * (S // 64) * H * D * 2
+    log(f"step {ms_per_step:.3f} ms (preprocess {pre_ms:.3f} ms, proxy forward {fwd_ms:.3f} ms)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import vsa_oracle as O
+        km_o, vs_o = O.vsa_preprocess(wl.k, wl.v, wl.vbs)   # the oracle's own summaries (not timed)
+        cpu = cpu_baseline_proxy(wl, km_o, vs_o, 4000)
+    rec = {
+        "metric": "VSA proxy-compensated fwd ms/call + effective TFLOP/s, packed [512 prefix | 624-cube video], H56",
+        "value": round((f_exact + f_proxy) / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description, "config": cfg.name, "batch": B, "heads": H,
+                   "seq_len": S, "prefix_len": cfg.prefix_len, "head_dim": D,
+                   "max_sel": int(wl.sel_idx.shape[-1]), "exact_flop": f_exact, "proxy_flop": f_proxy,
+                   "seed": wl.meta["seed"]},
+        "kernels_ms": {"preprocess_avg": round(pre_ms, 4), "proxy_forward_call_avg": round(fwd_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round((f_exact + f_proxy) / (fwd_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round((f_exact + f_proxy) / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "note": "whole vsa_fwd_proxy call (V and vsum packing included)"},
+        "preprocess_roofline": {"bound": "hbm", "achieved": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                                "peak": 8000.0, "unit": "GB/s",
+                                "frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / 8000.0, 4),
+                                "algorithmic_bytes": pre_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,8 +241,8 @@ def main():
         return
     cfg = W.CONFIGS[args.config]
     if cfg.proxy:
-        log("the headline benchmark uses a plain (non-proxy) configuration")
-        sys.exit(2)
+        bench_proxy(args, cfg, dev)
+        return
     t0 = time.perf_counter()
     wl = W.generate(cfg)
     log(f"generated config {cfg.name} in {time.perf_counter() - t0:.1f} s")
