@@ -40,7 +40,8 @@ import numpy as np
 BLOCK = 64
 
 __all__ = ["bf16_to_f64", "f64_to_bf16", "vsa_fwd", "vsa_fwd_item", "vsa_preprocess",
-           "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots"]
+           "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots", "cube_layout", "cube_tile",
+           "cube_untile"]
 
 
 # --------------------------------------------------------------------------
@@ -238,3 +239,51 @@ def vsa_fwd_proxy(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale, item
         o = vsa_fwd_proxy_item(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale, b, h, c)
         out[b, BLOCK * c:BLOCK * c + o.shape[0], h, :] = o
     return out
+
+
+# --------------------------------------------------------------------------
+# cube tiling of a latent video grid
+# --------------------------------------------------------------------------
+CUBE = 4
+
+
+def cube_layout(T: int, Hh: int, W: int):
+    """Cube-major layout of a T x Hh x W latent grid (Wan2.2 card, "Shapes").
+
+    The grid is cut into 4 x 4 x 4 cubes of 64 slots, ceil(T/4) x ceil(Hh/4) x
+    ceil(W/4) of them, numbered row-major over the cube grid.  Inside a cube the
+    real tokens keep their row-major (t, h, w) order and fill the first vbs[c]
+    slots; the remaining slots are padding.  Returns (slot, vbs): slot[n] is
+    the padded row of natural token n = (t * Hh + h) * W + w, vbs[c] the number
+    of real tokens of cube c.  Written out with plain loops over the cubes.
+    """
+    ct, ch, cw = -(-T // CUBE), -(-Hh // CUBE), -(-W // CUBE)
+    slot = np.full(T * Hh * W, -1, dtype=np.int64)
+    vbs = np.zeros(ct * ch * cw, dtype=np.int64)
+    for a in range(ct):
+        for b in range(ch):
+            for c in range(cw):
+                cube = (a * ch + b) * cw + c
+                r = 0
+                for t in range(CUBE * a, min(CUBE * a + CUBE, T)):
+                    for h in range(CUBE * b, min(CUBE * b + CUBE, Hh)):
+                        for w in range(CUBE * c, min(CUBE * c + CUBE, W)):
+                            slot[(t * Hh + h) * W + w] = BLOCK * cube + r
+                            r += 1
+                vbs[cube] = r
+    return slot, vbs
+
+
+def cube_tile(x, T: int, Hh: int, W: int):
+    """Natural [B, T*Hh*W, ...] rows -> cube-major [B, 64 * cubes, ...], padding rows zero."""
+    slot, vbs = cube_layout(T, Hh, W)
+    x = np.asarray(x)
+    out = np.zeros((x.shape[0], BLOCK * vbs.size) + x.shape[2:], dtype=x.dtype)
+    out[:, slot] = x
+    return out
+
+
+def cube_untile(xt, T: int, Hh: int, W: int):
+    """Cube-major rows -> natural [B, T*Hh*W, ...] rows (padding rows dropped)."""
+    slot, _ = cube_layout(T, Hh, W)
+    return np.asarray(xt)[:, slot]

@@ -335,3 +335,58 @@ def test_wan_shapes_from_the_pages():
     assert np.all(slot % 64 < vbs[slot // 64])
     cfg = W.CONFIGS["2"]
     assert cfg.seq_len == g["s_padded"] and cfg.topk == g["topk"] and cfg.heads == g["heads"]
+
+
+# --------------------------------------------------------------------------
+# cube tiling (Wan2.2 card, "Shapes")
+# --------------------------------------------------------------------------
+def test_cube_layout_hand_worked_5x5x5():
+    """A 5x5x5 grid: 2x2x2 cubes whose valid extents are 4 or 1 per axis."""
+    slot, vbs = O.cube_layout(5, 5, 5)
+    assert vbs.tolist() == [64, 16, 16, 4, 16, 4, 4, 1]
+    n = lambda t, h, w: (t * 5 + h) * 5 + w
+    assert slot[n(0, 0, 0)] == 0
+    assert slot[n(3, 3, 3)] == 63                 # last slot of the full cube
+    assert slot[n(0, 0, 4)] == 64                 # cube 1 = (0, 0, 1), extents 4x4x1
+    assert slot[n(1, 2, 4)] == 64 + 6             # rank (1 * 4 + 2) * 1 + 0
+    assert slot[n(4, 1, 2)] == 4 * 64 + 6         # cube 4 = (1, 0, 0), extents 1x4x4: rank 1*4+2
+    assert slot[n(4, 4, 4)] == 7 * 64             # the single token of the last cube
+
+
+def test_cube_layout_is_a_bijection_onto_valid_slots():
+    for grid in [(5, 6, 7), (21, 30, 52), (3, 4, 9)]:
+        slot, vbs = O.cube_layout(*grid)
+        valid = np.concatenate([64 * c + np.arange(v) for c, v in enumerate(vbs)])
+        assert np.array_equal(np.sort(slot), valid)
+        assert vbs.sum() == np.prod(grid)
+
+
+def test_cube_layout_of_the_wan_shapes():
+    g = json.load(open(os.path.join(GOLDEN, "wan_shapes.json")))
+    slot, vbs = O.cube_layout(*g["latent_grid"])
+    assert vbs.size == g["n_cubes"] and 64 * vbs.size == g["s_padded"]
+    assert vbs.sum() == g["real_tokens"]
+    # cube extents per axis: t 21 = 5*4 + 1, h 30 = 7*4 + 2, w 52 = 13*4
+    hist = dict(zip(*np.unique(vbs, return_counts=True)))
+    assert hist == {64: 5 * 7 * 13, 32: 5 * 1 * 13, 16: 1 * 7 * 13, 8: 1 * 1 * 13}
+
+
+def test_cube_tile_round_trip_and_zero_padding():
+    rng = np.random.default_rng(40)
+    T, Hh, W = 6, 5, 9
+    x = rng.integers(1, 2 ** 15, size=(2, T * Hh * W, 3, 8)).astype(np.uint16)
+    xt = O.cube_tile(x, T, Hh, W)
+    slot, vbs = O.cube_layout(T, Hh, W)
+    assert xt.shape == (2, 64 * vbs.size, 3, 8)
+    pad = np.ones(xt.shape[1], bool)
+    pad[slot] = False
+    assert not xt[:, pad].any()
+    assert np.array_equal(O.cube_untile(xt, T, Hh, W), x)
+
+
+def test_cube_layout_agrees_with_the_input_generator():
+    """The generator tiles its inputs with its own map; both readings must agree."""
+    for grid in [(5, 6, 7), (10, 15, 26), (21, 45, 80)]:
+        s_o, v_o = O.cube_layout(*grid)
+        s_w, v_w = W.tile_map(*grid)
+        assert np.array_equal(s_o, s_w) and np.array_equal(v_o, v_w)
