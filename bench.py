@@ -202,12 +202,69 @@ def bench_proxy(args, cfg, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_tile(args, cfg, dev):
+    """Cube tile + untile of one [B, T*H*W, heads, 128] bf16 tensor on the config's grid."""
+    import torch
+
+    import block_sparse_video_vsa_amd as vsa
+
+    B, H, D = cfg.batch, cfg.heads, 128
+    grid = cfg.grid
+    n = int(np.prod(grid))
+    cubes = len(vsa.cube_vbs(*grid))
+    g = torch.Generator(device=dev).manual_seed(cfg.seed)
+    x = torch.randn((B, n, H, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    xt = torch.empty((B, 64 * cubes, H, D), dtype=torch.bfloat16, device=dev)
+    back = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        vsa.vsa_tile(x, grid, out=xt)
+        vsa.vsa_untile(xt, grid, out=back)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        vsa.vsa_tile(x, grid, out=xt)
+        e[1].record(stream)
+        vsa.vsa_untile(xt, grid, out=back)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tile_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    untile_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    row = H * D * 2
+    tile_bytes = float(B * (n + 64 * cubes) * row)          # read natural rows, write every padded row
+    untile_bytes = float(B * 2 * n * row)                    # read valid padded rows, write natural rows
+    assert torch.equal(back, x), "untile(tile(x)) != x"
+    ms = wall * 1e3 / args.steps
+    rec = {
+        "metric": "cube tile + untile GB/s (algorithmic bytes), one bf16 [B, T*H*W, heads, 128] tensor",
+        "value": round((tile_bytes + untile_bytes) / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description, "grid": list(grid), "batch": B, "heads": H,
+                   "head_dim": D, "cubes": cubes},
+        "kernels_ms": {"tile_avg": round(tile_ms, 4), "untile_avg": round(untile_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(tile_bytes / (tile_ms * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(tile_bytes / (tile_ms * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "note": "tile kernel; untile " +
+                             f"{untile_bytes / (untile_ms * 1e-3) / 1e9:.0f} GB/s"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="2")
+    ap.add_argument("--op", default="attention", choices=["attention", "tile"],
+                    help="tile: time the cube tile/untile layout kernels on the config's grid")
     ap.add_argument("--cpu-items", type=int, default=4000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -240,6 +297,9 @@ def main():
         log(f"copied {args.copy_calibration_mib} MiB x {max(args.steps, 1)}")
         return
     cfg = W.CONFIGS[args.config]
+    if args.op == "tile":
+        bench_tile(args, cfg, dev)
+        return
     if cfg.proxy:
         bench_proxy(args, cfg, dev)
         return

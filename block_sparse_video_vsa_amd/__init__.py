@@ -3,6 +3,7 @@
 The computation lives in the HIP library libvsa.so (C ABI: include/vsa.h);
 `native` is its Python binding and `workloads` makes seeded synthetic inputs.
 """
-from .native import (VSAError, deterministic, fwd_workspace_size, get_deterministic,  # noqa: F401
-                     load_library, proxy_workspace_size, set_deterministic, vsa_fwd,
-                     vsa_fwd_prepacked, vsa_fwd_proxy, vsa_pack_values, vsa_preprocess)
+from .native import (VSAError, cube_vbs, deterministic, fwd_workspace_size,  # noqa: F401
+                     get_deterministic, load_library, proxy_workspace_size, set_deterministic,
+                     vsa_fwd, vsa_fwd_prepacked, vsa_fwd_proxy, vsa_pack_values, vsa_preprocess,
+                     vsa_tile, vsa_untile)

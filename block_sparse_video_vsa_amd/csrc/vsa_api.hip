@@ -289,3 +289,67 @@ extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
   if (launch_attn(p, true, s) != hipSuccess) return VSA_ERR_LAUNCH;
   return VSA_OK;
 }
+
+namespace {
+
+int64_t cube_count(int32_t T, int32_t Hh, int32_t W) {
+  if (T < 1 || Hh < 1 || W < 1) return 0;
+  const int64_t n = ((int64_t)T + 3) / 4 * (((int64_t)Hh + 3) / 4) * (((int64_t)W + 3) / 4);
+  if (n * kBlock >= ((int64_t)1 << 31)) return 0;
+  return n;
+}
+
+vsa_status check_tile(const void* a, const void* b, int32_t batch, int32_t T, int32_t Hh, int32_t W,
+                      int32_t num_heads, int32_t head_dim) {
+  if (!a || !b) return VSA_ERR_NULL;
+  if (batch < 1 || num_heads < 1 || head_dim < 1 || cube_count(T, Hh, W) == 0) return VSA_ERR_SHAPE;
+  if (((int64_t)num_heads * head_dim) % 8 != 0) return VSA_ERR_SHAPE;
+  const int64_t rows = (int64_t)batch * kBlock * cube_count(T, Hh, W);
+  if (rows >= ((int64_t)1 << 31)) return VSA_ERR_SHAPE;
+  if (!is_aligned(a, 16) || !is_aligned(b, 16)) return VSA_ERR_ALIGN;
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t vsa_cube_count(int32_t T, int32_t Hh, int32_t W) {
+  return (size_t)cube_count(T, Hh, W);
+}
+
+extern "C" vsa_status vsa_cube_vbs(int32_t T, int32_t Hh, int32_t W, int32_t* vbs_host, size_t n) {
+  if (!vbs_host) return VSA_ERR_NULL;
+  const int64_t cubes = cube_count(T, Hh, W);
+  if (cubes == 0 || (int64_t)n < cubes) return VSA_ERR_SHAPE;
+  const int ct = (T + 3) / 4, ch = (Hh + 3) / 4, cw = (W + 3) / 4;
+  for (int a = 0; a < ct; ++a)
+    for (int b = 0; b < ch; ++b)
+      for (int c = 0; c < cw; ++c) {
+        const int et = T - 4 * a < 4 ? T - 4 * a : 4;
+        const int eh = Hh - 4 * b < 4 ? Hh - 4 * b : 4;
+        const int ew = W - 4 * c < 4 ? W - 4 * c : 4;
+        vbs_host[(a * ch + b) * cw + c] = et * eh * ew;
+      }
+  return VSA_OK;
+}
+
+extern "C" vsa_status vsa_tile(const void* x, void* x_tiled, int32_t batch, int32_t T, int32_t Hh,
+                               int32_t W, int32_t num_heads, int32_t head_dim,
+                               vsa_stream_t stream) {
+  vsa_status st = check_tile(x, x_tiled, batch, T, Hh, W, num_heads, head_dim);
+  if (st != VSA_OK) return st;
+  return launch_tile(x, x_tiled, batch, T, Hh, W, (int64_t)num_heads * head_dim * 2, false,
+                     (hipStream_t)stream) == hipSuccess
+             ? VSA_OK
+             : VSA_ERR_LAUNCH;
+}
+
+extern "C" vsa_status vsa_untile(const void* x_tiled, void* x, int32_t batch, int32_t T, int32_t Hh,
+                                 int32_t W, int32_t num_heads, int32_t head_dim,
+                                 vsa_stream_t stream) {
+  vsa_status st = check_tile(x_tiled, x, batch, T, Hh, W, num_heads, head_dim);
+  if (st != VSA_OK) return st;
+  return launch_tile(x_tiled, x, batch, T, Hh, W, (int64_t)num_heads * head_dim * 2, true,
+                     (hipStream_t)stream) == hipSuccess
+             ? VSA_OK
+             : VSA_ERR_LAUNCH;
+}

@@ -62,6 +62,10 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+// Cube tiling (src natural rows -> dst cube-major padded rows) or, with untile,
+// its inverse (src cube-major -> dst natural); rows are row_bytes long.
+hipError_t launch_tile(const void* src, void* dst, int batch, int T, int Hh, int W, int64_t row_bytes,
+                       bool untile, hipStream_t stream);
 // Dynamic LDS bytes launch_attn requests for these parameters.
 size_t attn_dyn_lds(const AttnParams& p, bool proxy);
 

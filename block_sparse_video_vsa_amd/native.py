@@ -49,6 +49,12 @@ _SIGNATURES = {
     "vsa_fwd_proxy": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+    "vsa_cube_count": (_size_t, [_i32, _i32, _i32]),
+    "vsa_cube_vbs": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _size_t]),
+    "vsa_tile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _c_void_p]),
+    "vsa_untile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _c_void_p]),
 }
 
 VSA_OK = 0
@@ -118,6 +124,8 @@ def _stream(device: torch.device) -> int:
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in GPU memory (got {t.device})")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
@@ -263,4 +271,52 @@ def vsa_fwd_proxy(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale=None,
                            _default_scale(sm_scale), _ptr(workspace), workspace.numel(),
                            _stream(dev))
     _check("vsa_fwd_proxy", st)
+    return out
+
+
+def cube_vbs(T: int, Hh: int, W: int):
+    """Valid tokens per cube of a T x Hh x W grid (C ABI vsa_cube_vbs), numpy int32."""
+    import numpy as np
+    lib = load_library()
+    n = int(lib.vsa_cube_count(T, Hh, W))
+    if n == 0:
+        raise ValueError(f"grid {T}x{Hh}x{W} has no valid cube layout")
+    out = np.empty(n, dtype=np.int32)
+    _check("vsa_cube_vbs", lib.vsa_cube_vbs(T, Hh, W, out.ctypes.data, n))
+    return out
+
+
+def vsa_tile(x, grid, out=None):
+    """Natural [B, T*Hh*W, H, D] rows -> cube-major [B, 64*cubes, H, D] (C ABI vsa_tile)."""
+    lib = load_library()
+    T, Hh, W = grid
+    B, N, H, D = x.shape
+    if N != T * Hh * W:
+        raise ValueError(f"x has {N} rows, grid {T}x{Hh}x{W} has {T * Hh * W}")
+    cubes = int(lib.vsa_cube_count(T, Hh, W))
+    if out is None:
+        out = torch.empty((B, BLOCK * cubes, H, D), dtype=x.dtype, device=x.device)
+    _need(x, "x", x.dtype, x.device)
+    _need(out, "out", x.dtype, x.device, (B, BLOCK * cubes, H, D))
+    if x.element_size() != 2:
+        raise ValueError("vsa_tile moves 16-bit elements")
+    _check("vsa_tile", lib.vsa_tile(_ptr(x), _ptr(out), B, T, Hh, W, H, D, _stream(x.device)))
+    return out
+
+
+def vsa_untile(xt, grid, out=None):
+    """Cube-major [B, 64*cubes, H, D] rows -> natural [B, T*Hh*W, H, D] (C ABI vsa_untile)."""
+    lib = load_library()
+    T, Hh, W = grid
+    B, S, H, D = xt.shape
+    cubes = int(lib.vsa_cube_count(T, Hh, W))
+    if S != BLOCK * cubes:
+        raise ValueError(f"x_tiled has {S} rows, grid {T}x{Hh}x{W} needs {BLOCK * cubes}")
+    if out is None:
+        out = torch.empty((B, T * Hh * W, H, D), dtype=xt.dtype, device=xt.device)
+    _need(xt, "x_tiled", xt.dtype, xt.device)
+    _need(out, "out", xt.dtype, xt.device, (B, T * Hh * W, H, D))
+    if xt.element_size() != 2:
+        raise ValueError("vsa_untile moves 16-bit elements")
+    _check("vsa_untile", lib.vsa_untile(_ptr(xt), _ptr(out), B, T, Hh, W, H, D, _stream(xt.device)))
     return out

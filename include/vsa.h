@@ -182,6 +182,34 @@ vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
                          float sm_scale, void* workspace, size_t workspace_bytes,
                          vsa_stream_t stream);
 
+/*
+ * Cube tiling of a latent video grid ([SH]: 4 x 4 x 4 cubes of 64 tokens,
+ * padded to 64 * cubes rows).  The grid T x Hh x W has ceil(T/4) * ceil(Hh/4) *
+ * ceil(W/4) cubes, numbered row-major over the cube grid; inside a cube the real
+ * tokens keep their row-major (t, h, w) order and fill the first vbs[c] slots
+ * (vbs[c] = product of the cube's valid extents), the rest being padding.
+ *
+ * vsa_cube_count   number of cubes, or 0 if an extent is < 1 or the padded
+ *                  length would reach 2^31 rows.
+ * vsa_cube_vbs     fills vbs_host[0 .. cubes-1] (HOST memory, n >= cubes
+ *                  entries); VSA_ERR_NULL / VSA_ERR_SHAPE otherwise.
+ * vsa_tile         x [batch, T*Hh*W, num_heads, head_dim] (natural order
+ *                  n = (t*Hh + h)*W + w) -> x_tiled [batch, 64*cubes, num_heads,
+ *                  head_dim]; padding rows are written as zeros.
+ * vsa_untile       the inverse gather: x_tiled -> x (padding rows are ignored).
+ *
+ * Elements are 16-bit (bf16 here, but the copy is bit-exact for any 2-byte
+ * type); num_heads * head_dim must be a multiple of 8 (16-byte rows pieces) and
+ * both pointers 16-byte aligned (VSA_ERR_ALIGN otherwise).  Device memory,
+ * caller-owned, enqueued on `stream`; x and x_tiled must not overlap.
+ */
+size_t vsa_cube_count(int32_t T, int32_t Hh, int32_t W);
+vsa_status vsa_cube_vbs(int32_t T, int32_t Hh, int32_t W, int32_t* vbs_host, size_t n);
+vsa_status vsa_tile(const void* x, void* x_tiled, int32_t batch, int32_t T, int32_t Hh, int32_t W,
+                    int32_t num_heads, int32_t head_dim, vsa_stream_t stream);
+vsa_status vsa_untile(const void* x_tiled, void* x, int32_t batch, int32_t T, int32_t Hh, int32_t W,
+                      int32_t num_heads, int32_t head_dim, vsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"vsa_fwd", "vsa_preprocess", "vsa_fwd_proxy", "vsa_status_string",
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
-            "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic"} <= set(names)
+            "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
+            "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -121,3 +122,31 @@ def test_binding_rejects_cpu_tensors():
     vbs = torch.zeros(1, dtype=torch.int32)
     with pytest.raises((ValueError, TypeError, RuntimeError, AssertionError)):
         native.vsa_fwd(q, q, q, idx, vbs, out=q)
+
+
+def test_cube_count_and_vbs_match_the_oracle(lib):
+    """vsa_cube_vbs runs on the host: compare it with the oracle's layout directly."""
+    import numpy as np
+    from oracle import vsa_oracle as O
+    for grid in [(5, 5, 5), (21, 30, 52), (21, 45, 80), (1, 1, 1), (4, 4, 4), (9, 2, 13)]:
+        _, vbs_o = O.cube_layout(*grid)
+        assert lib.vsa_cube_count(*grid) == vbs_o.size
+        assert np.array_equal(native.cube_vbs(*grid), vbs_o)
+    assert lib.vsa_cube_count(0, 4, 4) == 0
+    assert lib.vsa_cube_count(4, -1, 4) == 0
+    buf = (ctypes.c_int32 * 7)()
+    assert lib.vsa_cube_vbs(5, 5, 5, buf, 7) == SHAPE          # 8 cubes do not fit in 7
+    assert lib.vsa_cube_vbs(5, 5, 5, None, 8) == NULL
+
+
+def test_tile_rejects_bad_arguments_on_host(lib):
+    t = lambda **kw: lib.vsa_tile(kw.get("x", FAKE), kw.get("xt", FAKE), kw.get("B", 1), kw.get("T", 5),
+                                  kw.get("Hh", 5), kw.get("W", 5), kw.get("H", 2), kw.get("D", 128), None)
+    assert t(x=None) == NULL
+    assert t(xt=None) == NULL
+    assert t(B=0) == SHAPE
+    assert t(T=0) == SHAPE
+    assert t(H=1, D=4) == SHAPE                  # rows of 4 elements are not 16-byte pieces
+    assert t(x=FAKE + 8) == ALIGN
+    assert lib.vsa_untile(FAKE + 4, FAKE, 1, 5, 5, 5, 2, 128, None) == ALIGN
+    assert lib.vsa_untile(FAKE, FAKE, 1, 5, 5, 0, 2, 128, None) == SHAPE

@@ -346,3 +346,24 @@ def test_proxy_flat_softmax_full_shape(dev):
     g = Grade(g_rows, r_rows, ids)
     print(f"proxy flat softmax ({len(items)} items): {g}")
     assert g.ok(), str(g)
+
+
+@pytest.mark.parametrize("grid,B,H,D", [((5, 5, 5), 1, 2, 128), ((5, 6, 7), 2, 3, 64),
+                                       ((9, 2, 13), 1, 1, 8), ((21, 30, 52), 1, 40, 128)])
+def test_cube_tile_untile_bitwise(dev, grid, B, H, D):
+    """Tile and untile against the oracle's layout: exact bit patterns, zero padding."""
+    rng = np.random.default_rng(50 + H)
+    n = int(np.prod(grid))
+    x = rng.integers(0, 2 ** 16, size=(B, n, H, D), dtype=np.uint16)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    xt = vsa.vsa_tile(xd, grid)
+    back = vsa.vsa_untile(xt, grid)
+    torch.cuda.synchronize()
+    xt_h = xt.cpu().numpy().view(np.uint16)
+    assert np.array_equal(xt_h, O.cube_tile(x, *grid))
+    assert np.array_equal(back.cpu().numpy().view(np.uint16), x)
+    # untile of an arbitrary padded tensor ignores its padding rows
+    junk = rng.integers(0, 2 ** 16, size=xt_h.shape, dtype=np.uint16)
+    got = vsa.vsa_untile(torch.from_numpy(junk.view(np.int16)).to(dev), grid)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), O.cube_untile(junk, *grid))
