@@ -41,7 +41,7 @@ BLOCK = 64
 
 __all__ = ["bf16_to_f64", "f64_to_bf16", "vsa_fwd", "vsa_fwd_item", "vsa_preprocess",
            "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots", "cube_layout", "cube_tile",
-           "cube_untile"]
+           "cube_untile", "vsa_fwd_lse_item", "vsa_fwd_lse", "merge_partials"]
 
 
 # --------------------------------------------------------------------------
@@ -287,3 +287,67 @@ def cube_untile(xt, T: int, Hh: int, W: int):
     """Cube-major rows -> natural [B, T*Hh*W, ...] rows (padding rows dropped)."""
     slot, _ = cube_layout(T, Hh, W)
     return np.asarray(xt)[:, slot]
+
+
+# --------------------------------------------------------------------------
+# row statistics and the merge of partial results
+# --------------------------------------------------------------------------
+def vsa_fwd_lse_item(q, k, v, topk_idx, vbs, sm_scale, b: int, h: int, qc: int):
+    """fp64 (o, lse) of query cube qc: o as vsa_fwd_item, lse_i = log sum_j exp(s_ij).
+
+    s_ij = sm_scale * q_i . k_j over the item's key set (natural logarithm).  A
+    row with an empty key set gets lse = -inf (the log of an empty sum) and o = 0.
+    """
+    vbs = np.asarray(vbs)
+    nq = int(vbs[qc])
+    D = q.shape[-1]
+    slots = item_key_slots(topk_idx[b, h, qc], vbs)
+    if nq == 0 or slots.size == 0:
+        return np.zeros((nq, D)), np.full(nq, -np.inf)
+    qm = bf16_to_f64(q[b, BLOCK * qc:BLOCK * qc + nq, h, :])
+    km = bf16_to_f64(k[b, slots, h, :])
+    vm = bf16_to_f64(v[b, slots, h, :])
+    s = (qm @ km.T) * float(np.float32(sm_scale))
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    tot = e.sum(axis=1)
+    return (e @ vm) / tot[:, None], m[:, 0] + np.log(tot)
+
+
+def vsa_fwd_lse(q, k, v, topk_idx, vbs, sm_scale, items=None):
+    """fp64 (o [B, S, H, D], lse [B, H, S]); padding rows: o = 0, lse = -inf."""
+    B, S, H, D = q.shape
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    lse = np.full((B, H, S), -np.inf)
+    if items is None:
+        items = [(b, h, c) for b in range(B) for h in range(H) for c in range(S // BLOCK)]
+    for b, h, c in items:
+        o, l = vsa_fwd_lse_item(q, k, v, topk_idx, vbs, sm_scale, b, h, c)
+        out[b, BLOCK * c:BLOCK * c + o.shape[0], h, :] = o
+        lse[b, h, BLOCK * c:BLOCK * c + l.size] = l
+    return out, lse
+
+
+def merge_partials(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint key sets from the two partial results.
+
+    With lse_k = log sum over set k of exp(s) and o_k the softmax average over
+    set k, the union has lse = log(exp(lse1) + exp(lse2)) and
+    o = (exp(lse1 - lse) o1 + exp(lse2 - lse) o2).  o are float arrays
+    [..., D] (widen bf16 first), lse the matching [...] arrays; rows where both
+    parts are empty (-inf) give o = 0 and lse = -inf.  float64 throughout.
+    """
+    o1 = np.asarray(o1, np.float64)
+    o2 = np.asarray(o2, np.float64)
+    l1 = np.asarray(lse1, np.float64)
+    l2 = np.asarray(lse2, np.float64)
+    m = np.maximum(l1, l2)
+    empty = np.isneginf(m)
+    ms = np.where(empty, 0.0, m)
+    w1 = np.where(np.isneginf(l1), 0.0, np.exp(l1 - ms))
+    w2 = np.where(np.isneginf(l2), 0.0, np.exp(l2 - ms))
+    tot = w1 + w2
+    lse = np.where(empty, -np.inf, ms + np.log(np.where(empty, 1.0, tot)))
+    den = np.where(empty, 1.0, tot)[..., None]
+    o = (w1[..., None] * o1 + w2[..., None] * o2) / den
+    return np.where(empty[..., None], 0.0, o), lse

@@ -390,3 +390,81 @@ def test_cube_layout_agrees_with_the_input_generator():
         s_o, v_o = O.cube_layout(*grid)
         s_w, v_w = W.tile_map(*grid)
         assert np.array_equal(s_o, s_w) and np.array_equal(v_o, v_w)
+
+
+# --------------------------------------------------------------------------
+# row statistics and merge
+# --------------------------------------------------------------------------
+def test_lse_is_the_log_of_the_softmax_normaliser():
+    """lse against a pure-Python log-sum of exponentials, and o unchanged."""
+    rng = np.random.default_rng(60)
+    wl = W.generate("0")
+    o64 = O.vsa_fwd(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+    o, lse = O.vsa_fwd_lse(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+    assert np.max(np.abs(o - o64)) <= 1e-14 * np.max(np.abs(o64))   # same values, other rounding order
+    scale = float(np.float32(wl.sm_scale))
+    for _ in range(5):
+        h = int(rng.integers(wl.q.shape[2]))
+        c = int(rng.integers(wl.q.shape[1] // 64))
+        slots = O.item_key_slots(wl.topk_idx[0, h, c], wl.vbs)
+        for r in range(int(wl.vbs[c])):
+            qi = O.bf16_to_f64(wl.q[0, 64 * c + r, h])
+            logits = [scale * float(sum(qi[d] * O.bf16_to_f64(wl.k[0, s, h, d]) for d in range(128)))
+                      for s in slots]
+            ref = math.log(sum(math.exp(x) for x in logits)) if logits else -math.inf
+            assert abs(lse[0, h, 64 * c + r] - ref) <= 1e-12 * max(1.0, abs(ref))
+    pad = np.ones(wl.q.shape[1], bool)
+    pad[wl.valid_slots] = False
+    assert np.all(np.isneginf(lse[:, :, pad]))
+
+
+def test_lse_single_key_is_its_logit_and_empty_is_minus_infinity():
+    vbs = np.array([1, 0, 64], np.int32)
+    rng = np.random.default_rng(61)
+    q, k, v = (W.f32_to_bf16_bits(rng.standard_normal((1, 192, 1, 128)).astype(np.float32))
+               for _ in range(3))
+    idx = np.array([[[[0], [0], [1]]]], np.int32)        # cube 2 selects only the empty cube 1
+    o, lse = O.vsa_fwd_lse(q, k, v, idx, vbs, np.float32(0.125))
+    s0 = 0.125 * float(O.bf16_to_f64(q[0, 0, 0]) @ O.bf16_to_f64(k[0, 0, 0]))
+    assert abs(lse[0, 0, 0] - s0) <= 1e-12 * max(1.0, abs(s0))
+    assert np.all(np.isneginf(lse[0, 0, 128:])) and not o[0, 128:].any()
+
+
+def test_merge_of_disjoint_parts_equals_attention_over_the_union():
+    """Split each index row in two, attend to each part, merge: the full result."""
+    wl = W.generate("1")
+    rng = np.random.default_rng(62)
+    T = wl.topk_idx
+    perm = np.argsort(rng.random(T.shape), axis=-1)
+    Ts = np.take_along_axis(T, perm, axis=-1)
+    cut = T.shape[-1] // 2
+    items = [(0, h, c) for h in range(2) for c in range(0, T.shape[2], 7)]
+    o_full, lse_full = O.vsa_fwd_lse(wl.q, wl.k, wl.v, T, wl.vbs, wl.sm_scale, items)
+    o1, l1 = O.vsa_fwd_lse(wl.q, wl.k, wl.v, Ts[..., :cut], wl.vbs, wl.sm_scale, items)
+    o2, l2 = O.vsa_fwd_lse(wl.q, wl.k, wl.v, Ts[..., cut:], wl.vbs, wl.sm_scale, items)
+    om, lm = O.merge_partials(o1, np.moveaxis(l1, 1, 2), o2, np.moveaxis(l2, 1, 2))
+    lm = np.moveaxis(lm, 2, 1)
+    fin = np.isfinite(lse_full)
+    assert np.array_equal(fin, np.isfinite(lm))
+    assert np.max(np.abs(lm[fin] - lse_full[fin])) <= 1e-12 * np.max(np.abs(lse_full[fin]))
+    assert np.max(np.abs(om - o_full)) <= 1e-12 * max(1.0, np.max(np.abs(o_full)))
+
+
+def test_merge_with_an_empty_part_and_symmetry():
+    rng = np.random.default_rng(63)
+    o1 = rng.standard_normal((5, 7, 16))
+    l1 = rng.standard_normal((5, 7)) * 30
+    o2 = rng.standard_normal((5, 7, 16))
+    l2 = rng.standard_normal((5, 7)) * 30
+    e = np.full((5, 7), -np.inf)
+    om, lm = O.merge_partials(o1, l1, np.zeros_like(o2), e)
+    assert np.array_equal(lm, l1) and np.allclose(om, o1, rtol=0, atol=0)
+    a, la = O.merge_partials(o1, l1, o2, l2)
+    b, lb = O.merge_partials(o2, l2, o1, l1)
+    assert np.allclose(a, b, rtol=1e-15, atol=1e-15) and np.allclose(la, lb, rtol=1e-15, atol=0)
+    z, lz = O.merge_partials(o1, e, o2, e)
+    assert np.all(np.isneginf(lz)) and not z.any()
+    # equal weights give the midpoint and log 2 more
+    m, lmid = O.merge_partials(o1, l1, o2, l1)
+    assert np.allclose(m, (o1 + o2) / 2, rtol=1e-15, atol=1e-15)
+    assert np.allclose(lmid, l1 + math.log(2.0), rtol=1e-15, atol=1e-13)
