@@ -257,14 +257,58 @@ def bench_tile(args, cfg, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_merge(args, cfg, dev):
+    """vsa_merge of two bf16 [B, S, H, 128] partial results with their fp32 [B, H, S] lse."""
+    import torch
+
+    import block_sparse_video_vsa_amd as vsa
+
+    B, H, D = cfg.batch, cfg.heads, 128
+    S = cfg.seq_len
+    g = torch.Generator(device=dev).manual_seed(cfg.seed)
+    o1, o2 = (torch.randn((B, S, H, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    l1, l2 = (torch.randn((B, H, S), generator=g, device=dev) * 10 for _ in range(2))
+    out = torch.empty_like(o1)
+    lo = torch.empty_like(l1)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        vsa.vsa_merge(o1, l1, o2, l2, out, lo)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        vsa.vsa_merge(o1, l1, o2, l2, out, lo)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = float(3 * B * S * H * D * 2 + 3 * B * H * S * 4)
+    rec = {
+        "metric": "merge of two partial attention results GB/s (algorithmic bytes)",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.description, "batch": B, "seq_len": S, "heads": H, "head_dim": D},
+        "kernels_ms": {"merge_avg": round(k_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (k_ms * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(nbytes / (k_ms * 1e-3) / 1e9 / 8000.0, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="2")
-    ap.add_argument("--op", default="attention", choices=["attention", "tile"],
-                    help="tile: time the cube tile/untile layout kernels on the config's grid")
+    ap.add_argument("--op", default="attention", choices=["attention", "tile", "merge"],
+                    help="tile: the cube tile/untile layout kernels on the config's grid; "
+                         "merge: the merge of two partial results at the config's shape")
     ap.add_argument("--cpu-items", type=int, default=4000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -299,6 +343,9 @@ def main():
     cfg = W.CONFIGS[args.config]
     if args.op == "tile":
         bench_tile(args, cfg, dev)
+        return
+    if args.op == "merge":
+        bench_merge(args, cfg, dev)
         return
     if cfg.proxy:
         bench_proxy(args, cfg, dev)

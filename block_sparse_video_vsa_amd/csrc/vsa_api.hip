@@ -147,7 +147,7 @@ vsa_status enqueue_pack(const void* v, const int32_t* vbs, int32_t batch, int32_
 vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
                           const int32_t* vbs, void* out, int32_t batch, int32_t seq_len,
                           int32_t num_heads, int32_t topk, float sm_scale, void* workspace,
-                          hipStream_t s) {
+                          hipStream_t s, float* lse = nullptr) {
   const int nblk = seq_len / kBlock;
   const WsLayout ws = ws_layout(batch, num_heads, nblk, 0);
   uint8_t* wsb = (uint8_t*)workspace;
@@ -161,6 +161,7 @@ vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
   p.out = (uint16_t*)out;
   p.idx_width = topk;
   p.table_cap = topk;
+  p.lse = lse;
   return launch_attn(p, false, s) == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH;
 }
 
@@ -179,6 +180,40 @@ extern "C" vsa_status vsa_fwd(const void* q, const void* k, const void* v,
   if (st != VSA_OK) return st;
   return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
                         workspace, s);
+}
+
+extern "C" vsa_status vsa_fwd_lse(const void* q, const void* k, const void* v,
+                                  const int32_t* topk_idx, const int32_t* vbs, void* out,
+                                  float* lse, int32_t batch, int32_t seq_len, int32_t num_heads,
+                                  int32_t head_dim, int32_t topk, float sm_scale, void* workspace,
+                                  size_t workspace_bytes, vsa_stream_t stream) {
+  if (!lse) return VSA_ERR_NULL;
+  vsa_status st = check_fwd(q, k, v, topk_idx, vbs, out, batch, seq_len, num_heads, head_dim,
+                            topk, sm_scale, workspace, workspace_bytes, true, true);
+  if (st != VSA_OK) return st;
+  if (!is_aligned(lse, 4)) return VSA_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  st = enqueue_pack(v, vbs, batch, seq_len, num_heads, workspace, s);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
+                        workspace, s, lse);
+}
+
+extern "C" vsa_status vsa_merge(const void* o1, const float* lse1, const void* o2,
+                                const float* lse2, void* out, float* lse_out, int32_t batch,
+                                int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                                vsa_stream_t stream) {
+  if (!o1 || !lse1 || !o2 || !lse2 || !out || !lse_out) return VSA_ERR_NULL;
+  if (batch < 1 || seq_len < 1 || num_heads < 1 || head_dim < 8 || head_dim % 8 != 0)
+    return VSA_ERR_SHAPE;
+  if ((int64_t)batch * seq_len * num_heads * head_dim >= ((int64_t)1 << 40)) return VSA_ERR_SHAPE;
+  if (!is_aligned(o1, 16) || !is_aligned(o2, 16) || !is_aligned(out, 16) || !is_aligned(lse1, 4) ||
+      !is_aligned(lse2, 4) || !is_aligned(lse_out, 4))
+    return VSA_ERR_ALIGN;
+  return launch_merge((const uint16_t*)o1, lse1, (const uint16_t*)o2, lse2, (uint16_t*)out, lse_out,
+                      batch, seq_len, num_heads, head_dim, (hipStream_t)stream) == hipSuccess
+             ? VSA_OK
+             : VSA_ERR_LAUNCH;
 }
 
 extern "C" vsa_status vsa_pack_values(const void* v, const int32_t* vbs, int32_t batch,

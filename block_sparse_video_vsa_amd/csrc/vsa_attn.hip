@@ -525,6 +525,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int r = i >> 4, c = i & 15;
       *(u32x4*)(out_rows + (int64_t)r * row_stride + c * 8) = (u32x4){0u, 0u, 0u, 0u};
     }
+    if (p.lse != nullptr && tid < kBlock) p.lse[(int64_t)bh * p.seq + (int64_t)qb * kBlock + tid] = -INFINITY;
     return;
   }
 
@@ -706,6 +707,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const float l_tot = pair_sum(st.lsum);
   const bool row_ok = active && qrow < vq && l_tot > 0.0f;
   const float inv = row_ok ? 1.0f / l_tot : 0.0f;
+  if (p.lse != nullptr && hh == 0) {
+    // natural log of the softmax normaliser: l sums 2^(s c - mc), so
+    // log sum exp(s * sm_scale) = (mc + log2 l) ln 2; -inf without keys.
+    p.lse[(int64_t)bh * p.seq + (int64_t)qb * kBlock + qrow] =
+        row_ok ? (st.mc + log2f(l_tot)) * 0.693147180559945f : -INFINITY;
+  }
   uint16_t* orow = out_rows + (int64_t)qrow * row_stride + 4 * hh;
   auto store4 = [&](const f32x16& acc, int db) {
 #pragma unroll

@@ -43,6 +43,7 @@ struct AttnParams {
   const int32_t* idx;       // topk_idx [B,H,Nq,topk] or sel_idx [B,H,Nv,max_sel]
   const int32_t* vbs;
   uint16_t* out;
+  float* lse;               // optional [B, H, S] row log-sum-exp (nullptr: none)
   int batch, seq, heads, nblk;
   int idx_width;            // topk or max_sel
   int nprefix;              // prefix blocks (proxy mode)
@@ -62,6 +63,10 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+// Merge of two partial attention results over disjoint key sets.
+hipError_t launch_merge(const uint16_t* o1, const float* lse1, const uint16_t* o2, const float* lse2,
+                        uint16_t* out, float* lse_out, int batch, int seq, int heads, int head_dim,
+                        hipStream_t stream);
 // Cube tiling (src natural rows -> dst cube-major padded rows) or, with untile,
 // its inverse (src cube-major -> dst natural); rows are row_bytes long.
 hipError_t launch_tile(const void* src, void* dst, int batch, int T, int Hh, int W, int64_t row_bytes,

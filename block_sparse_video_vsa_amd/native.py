@@ -49,6 +49,11 @@ _SIGNATURES = {
     "vsa_fwd_proxy": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+    "vsa_fwd_lse": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32,
+                                   _c_void_p, _size_t, _c_void_p]),
+    "vsa_merge": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _i32, _i32, _i32, _i32, _c_void_p]),
     "vsa_cube_count": (_size_t, [_i32, _i32, _i32]),
     "vsa_cube_vbs": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _size_t]),
     "vsa_tile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -320,3 +325,51 @@ def vsa_untile(xt, grid, out=None):
         raise ValueError("vsa_untile moves 16-bit elements")
     _check("vsa_untile", lib.vsa_untile(_ptr(xt), _ptr(out), B, T, Hh, W, H, D, _stream(xt.device)))
     return out
+
+
+def vsa_fwd_lse(q, k, v, topk_idx, vbs, sm_scale=None, out=None, lse=None, workspace=None):
+    """Forward plus row log-sum-exp (C ABI vsa_fwd_lse): returns (out, lse [B, H, S] float32)."""
+    lib = load_library()
+    dev = q.device
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev, (B, S, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    if topk_idx.dim() != 4 or tuple(topk_idx.shape[:3]) != (B, H, S // BLOCK):
+        raise ValueError(f"topk_idx has shape {tuple(topk_idx.shape)}, expected (B, H, S/64, topk)")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (B, S, H, D))
+    _need(lse, "lse", torch.float32, dev, (B, H, S))
+    nbytes = fwd_workspace_size(B, S, H, D)
+    if workspace is None:
+        workspace = _workspace(dev, max(nbytes, 1))
+    st = lib.vsa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(vbs), _ptr(out), _ptr(lse),
+                         B, S, H, D, topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
+                         workspace.numel(), _stream(dev))
+    _check("vsa_fwd_lse", st)
+    return out, lse
+
+
+def vsa_merge(o1, lse1, o2, lse2, out=None, lse_out=None):
+    """Combine two partial results over disjoint key sets (C ABI vsa_merge)."""
+    lib = load_library()
+    dev = o1.device
+    B, S, H, D = o1.shape
+    _need(o1, "o1", torch.bfloat16, dev)
+    _need(o2, "o2", torch.bfloat16, dev, (B, S, H, D))
+    _need(lse1, "lse1", torch.float32, dev, (B, H, S))
+    _need(lse2, "lse2", torch.float32, dev, (B, H, S))
+    if out is None:
+        out = torch.empty_like(o1)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse1)
+    _need(out, "out", torch.bfloat16, dev, (B, S, H, D))
+    _need(lse_out, "lse_out", torch.float32, dev, (B, H, S))
+    st = lib.vsa_merge(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), _ptr(out), _ptr(lse_out),
+                       B, S, H, D, _stream(dev))
+    _check("vsa_merge", st)
+    return out, lse_out

@@ -183,6 +183,44 @@ vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
                          vsa_stream_t stream);
 
 /*
+ * vsa_fwd_lse -- vsa_fwd that also returns the row statistics.
+ *
+ *   lse           float32 [batch, num_heads, seq_len] output, 4-byte aligned:
+ *                 for each valid query row the natural log of its softmax
+ *                 normaliser, log sum_j exp(sm_scale * q . k_j) over the row's
+ *                 keys; -inf for padding rows and rows with no valid key.
+ *   other arguments, outputs and errors as vsa_fwd.
+ *
+ * With lse, results over disjoint key sets of the same rows can be combined
+ * exactly (vsa_merge) -- splitting a long key list, or joining this output
+ * with another attention branch over the same queries.
+ */
+vsa_status vsa_fwd_lse(const void* q, const void* k, const void* v,
+                       const int32_t* topk_idx, const int32_t* vbs, void* out, float* lse,
+                       int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                       int32_t topk, float sm_scale,
+                       void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+
+/*
+ * vsa_merge -- attention over the union of two disjoint key sets from the two
+ * partial results: lse = log(exp(lse1) + exp(lse2)),
+ * out = exp(lse1 - lse) o1 + exp(lse2 - lse) o2 (fp32, rounded once to bf16,
+ * nearest even).  Rows where both parts are empty (-inf) get out = 0 and
+ * lse_out = -inf.
+ *
+ *   o1, o2, out   bf16 [batch, seq_len, num_heads, head_dim], 16-byte aligned;
+ *                 out may be o1 or o2 (each piece is read before it is written).
+ *   lse1, lse2    float32 [batch, num_heads, seq_len], 4-byte aligned.
+ *   lse_out       float32 [batch, num_heads, seq_len]; must not overlap lse1 or
+ *                 lse2.
+ *   head_dim      a positive multiple of 8 (any head geometry: a pure
+ *                 elementwise step).
+ */
+vsa_status vsa_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                     void* out, float* lse_out, int32_t batch, int32_t seq_len,
+                     int32_t num_heads, int32_t head_dim, vsa_stream_t stream);
+
+/*
  * Cube tiling of a latent video grid ([SH]: 4 x 4 x 4 cubes of 64 tokens,
  * padded to 64 * cubes rows).  The grid T x Hh x W has ceil(T/4) * ceil(Hh/4) *
  * ceil(W/4) cubes, numbered row-major over the cube grid; inside a cube the real

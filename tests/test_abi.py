@@ -30,7 +30,8 @@ def test_every_declared_function_is_exported(lib):
     assert {"vsa_fwd", "vsa_preprocess", "vsa_fwd_proxy", "vsa_status_string",
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
             "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
-            "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile"} <= set(names)
+            "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
+            "vsa_merge"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -150,3 +151,19 @@ def test_tile_rejects_bad_arguments_on_host(lib):
     assert t(x=FAKE + 8) == ALIGN
     assert lib.vsa_untile(FAKE + 4, FAKE, 1, 5, 5, 5, 2, 128, None) == ALIGN
     assert lib.vsa_untile(FAKE, FAKE, 1, 5, 5, 0, 2, 128, None) == SHAPE
+
+
+def test_lse_and_merge_reject_bad_arguments_on_host(lib):
+    f = lambda lse=FAKE, **kw: lib.vsa_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lse, 1, 512, 2, 128,
+                                               kw.get("topk", 2), 0.088, FAKE, 1 << 30, None)
+    assert f(lse=None) == NULL
+    assert f(topk=0) == SHAPE
+    assert f(lse=FAKE + 2) == ALIGN
+    m = lambda **kw: lib.vsa_merge(kw.get("o1", FAKE), kw.get("l1", FAKE), FAKE, FAKE, FAKE,
+                                   kw.get("lo", FAKE), 1, kw.get("S", 64), 2, kw.get("D", 128), None)
+    assert m(o1=None) == NULL
+    assert m(lo=None) == NULL
+    assert m(D=12) == SHAPE
+    assert m(S=0) == SHAPE
+    assert m(o1=FAKE + 8) == ALIGN
+    assert m(l1=FAKE + 2) == ALIGN

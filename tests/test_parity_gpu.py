@@ -367,3 +367,111 @@ def test_cube_tile_untile_bitwise(dev, grid, B, H, D):
     got = vsa.vsa_untile(torch.from_numpy(junk.view(np.int16)).to(dev), grid)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy().view(np.uint16), O.cube_untile(junk, *grid))
+
+
+# --------------------------------------------------------------------------
+# row statistics and merge
+# --------------------------------------------------------------------------
+# The kernel's row sum l takes the fp16 (round toward zero) probabilities that
+# feed the PV product, each at most 2^-10 below its exact value, and the lazy
+# rescale keeps l in fp32: log l may sit up to about 2^-10 below the exact
+# value.  Bound used: |lse_gpu - lse_64| <= 2e-3 + 1e-6 |lse|.
+LSE_TOL = 2e-3
+
+
+def _lse_ok(lse_gpu, lse64):
+    fin = np.isfinite(lse64)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), "finite pattern differs"
+    assert np.all(np.isneginf(lse_gpu[~fin]))
+    d = np.abs(lse_gpu[fin] - lse64[fin])
+    assert np.all(d <= LSE_TOL + 1e-6 * np.abs(lse64[fin])), f"max |d lse| {d.max():.3g}"
+    return float(d.max()) if d.size else 0.0
+
+
+@pytest.mark.parametrize("name", ["0", "1"])
+def test_lse_small_configs_full(dev, name):
+    wl = W.generate(name)
+    args = [to_dev(wl.q, dev, True), to_dev(wl.k, dev, True), to_dev(wl.v, dev, True),
+            to_dev(wl.topk_idx, dev), to_dev(wl.vbs, dev)]
+    with vsa.deterministic():
+        out, lse = vsa.vsa_fwd_lse(*args, float(wl.sm_scale))
+        plain = vsa.vsa_fwd(*args, float(wl.sm_scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), from_dev(plain))      # same output as vsa_fwd
+    o64, l64 = O.vsa_fwd_lse(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+    g = grade_full(from_dev(out), o64, wl.vbs)
+    assert g.ok(), str(g)
+    dmax = _lse_ok(lse.cpu().numpy(), l64)
+    print(f"config {name}: max |d lse| = {dmax:.3g}")
+
+
+def test_lse_config2_sampled(dev):
+    wl = W.generate("2")
+    out, lse = vsa.vsa_fwd_lse(to_dev(wl.q, dev, True), to_dev(wl.k, dev, True),
+                               to_dev(wl.v, dev, True), to_dev(wl.topk_idx, dev), to_dev(wl.vbs, dev),
+                               float(wl.sm_scale))
+    torch.cuda.synchronize()
+    lse = lse.cpu().numpy()
+    items = sample_items(wl, 24, seed=8)
+    worst = 0.0
+    for b, h, c in items:
+        _, l64 = O.vsa_fwd_lse_item(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale, b, h, c)
+        n = l64.size
+        worst = max(worst, _lse_ok(lse[b, h, 64 * c:64 * c + n], l64))
+        assert np.all(np.isneginf(lse[b, h, 64 * c + n:64 * c + 64]))
+    print(f"config 2 (24 sampled items): max |d lse| = {worst:.3g}")
+
+
+def test_split_and_merge_equals_the_whole_row(dev):
+    """Each index row split in two disjoint parts, attended separately and merged."""
+    wl = W.generate("1")
+    rng = np.random.default_rng(64)
+    T = wl.topk_idx
+    Ts = np.take_along_axis(T, np.argsort(rng.random(T.shape), axis=-1), axis=-1)
+    cut = T.shape[-1] // 3
+    q, k, v = (to_dev(x, dev, True) for x in (wl.q, wl.k, wl.v))
+    vbs = to_dev(wl.vbs, dev)
+    o1, l1 = vsa.vsa_fwd_lse(q, k, v, to_dev(np.ascontiguousarray(Ts[..., :cut]), dev), vbs,
+                             float(wl.sm_scale))
+    o2, l2 = vsa.vsa_fwd_lse(q, k, v, to_dev(np.ascontiguousarray(Ts[..., cut:]), dev), vbs,
+                             float(wl.sm_scale))
+    om, lm = vsa.vsa_merge(o1, l1, o2, l2)
+    torch.cuda.synchronize()
+    o64, l64 = O.vsa_fwd_lse(wl.q, wl.k, wl.v, T, wl.vbs, wl.sm_scale)
+    g = grade_full(from_dev(om), o64, wl.vbs)
+    print(f"split + merge: {g}")
+    # The merged rows are rounded to bf16 three times (each part, then the
+    # merge), so a value near a bf16 step may land one step away from the
+    # single rounding of the exact result (0.03125 for |o| in [4, 8)).  The
+    # 3e-2 bound is therefore applied against the exact (fp64) values here.
+    assert g.finite and g.min_cos >= 0.9999 and g.mean_abs <= 1e-4, str(g)
+    assert g.max_abs_unrounded <= 3e-2, str(g)
+    _lse_ok(lm.cpu().numpy(), l64)
+
+
+def test_merge_against_the_oracle(dev):
+    """vsa_merge on random parts, with empty parts on one side, the other, or both."""
+    rng = np.random.default_rng(65)
+    B, S, H, D = 2, 96, 3, 64
+    o1 = W.f32_to_bf16_bits(rng.standard_normal((B, S, H, D)).astype(np.float32))
+    o2 = W.f32_to_bf16_bits((3 * rng.standard_normal((B, S, H, D))).astype(np.float32))
+    l1 = (rng.standard_normal((B, H, S)) * 20).astype(np.float32)
+    l2 = (rng.standard_normal((B, H, S)) * 20).astype(np.float32)
+    l1[:, :, :10] = -np.inf
+    l2[:, :, 5:15] = -np.inf
+    out, lo = vsa.vsa_merge(to_dev(o1, dev, True), torch.from_numpy(l1).to(dev),
+                            to_dev(o2, dev, True), torch.from_numpy(l2).to(dev))
+    torch.cuda.synchronize()
+    om, lm = O.merge_partials(np.moveaxis(O.bf16_to_f64(o1), 2, 1), l1.astype(np.float64),
+                              np.moveaxis(O.bf16_to_f64(o2), 2, 1), l2.astype(np.float64))
+    ref = O.f64_to_bf16(np.moveaxis(om, 1, 2))
+    got = from_dev(out)
+    # fp32 arithmetic, one rounding: within one bf16 step of the rounded fp64 value
+    dg, dr = O.bf16_to_f64(got), O.bf16_to_f64(ref)
+    assert np.all(np.abs(dg - dr) <= 2.0 ** -7 * np.abs(dr) + 1e-30)
+    assert (got != ref).mean() < 0.01
+    lo = lo.cpu().numpy()
+    fin = np.isfinite(lm)
+    assert np.array_equal(np.isfinite(lo), fin) and np.all(np.isneginf(lo[~fin]))
+    assert np.all(np.abs(lo[fin] - lm[fin]) <= 1e-5 * (1 + np.abs(lm[fin])))
+    assert not got[:, 5:10].any()                      # both parts empty -> zeros
