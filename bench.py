@@ -137,6 +137,10 @@ def bench_proxy(args, cfg, dev):
 
     q, k, v = up(wl.q, True), up(wl.k, True), up(wl.v, True)
     sel, vbs = up(wl.sel_idx), up(wl.vbs)
+    width = int(wl.sel_idx.shape[-1])
+    nv = wl.sel_idx.shape[2]
+    mask = up(W.sel_to_bitmask(wl.sel_idx, nv)) if args.sel_format == "bitmask" else None
+    indptr, indices = (up(x) for x in W.sel_to_bsr(wl.sel_idx)) if args.sel_format == "bsr" else (None, None)
     km = torch.empty((B, S // 64, H, D), dtype=torch.bfloat16, device=dev)
     vs = torch.empty_like(km)
     out = torch.empty_like(q)
@@ -150,7 +154,14 @@ def bench_proxy(args, cfg, dev):
         vsa.vsa_preprocess(k, v, vbs, km, vs)
         if ev is not None:
             ev[1].record(stream)
-        vsa.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, cfg.prefix_len, scale, out=out, workspace=ws)
+        if args.sel_format == "bitmask":
+            vsa.vsa_fwd_proxy_bitmask(q, k, v, mask, vbs, km, vs, cfg.prefix_len, width, scale, out=out,
+                                      workspace=ws)
+        elif args.sel_format == "bsr":
+            vsa.vsa_fwd_proxy_bsr(q, k, v, indptr, indices, vbs, km, vs, cfg.prefix_len, width, scale,
+                                  out=out, workspace=ws)
+        else:
+            vsa.vsa_fwd_proxy(q, k, v, sel, vbs, km, vs, cfg.prefix_len, scale, out=out, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -185,6 +196,7 @@ def bench_proxy(args, cfg, dev):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.description, "config": cfg.name, "batch": B, "heads": H,
                    "seq_len": S, "prefix_len": cfg.prefix_len, "head_dim": D,
+                   "selection_format": args.sel_format,
                    "max_sel": int(wl.sel_idx.shape[-1]), "exact_flop": f_exact, "proxy_flop": f_proxy,
                    "seed": wl.meta["seed"]},
         "kernels_ms": {"preprocess_avg": round(pre_ms, 4), "proxy_forward_call_avg": round(fwd_ms, 4)},
@@ -306,6 +318,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="2")
+    ap.add_argument("--sel-format", default="padded", choices=["padded", "bitmask", "bsr"],
+                    help="proxy workload: encoding of the exact-block selection")
     ap.add_argument("--op", default="attention", choices=["attention", "tile", "merge"],
                     help="tile: the cube tile/untile layout kernels on the config's grid; "
                          "merge: the merge of two partial results at the config's shape")

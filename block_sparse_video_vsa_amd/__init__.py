@@ -5,5 +5,6 @@ The computation lives in the HIP library libvsa.so (C ABI: include/vsa.h);
 """
 from .native import (VSAError, cube_vbs, deterministic, fwd_workspace_size,  # noqa: F401
                      get_deterministic, load_library, proxy_workspace_size, set_deterministic,
-                     vsa_fwd, vsa_fwd_lse, vsa_fwd_prepacked, vsa_fwd_proxy, vsa_merge,
+                     vsa_fwd, vsa_fwd_lse, vsa_fwd_prepacked, vsa_fwd_proxy,
+                     vsa_fwd_proxy_bitmask, vsa_fwd_proxy_bsr, vsa_merge,
                      vsa_pack_values, vsa_preprocess, vsa_tile, vsa_untile)

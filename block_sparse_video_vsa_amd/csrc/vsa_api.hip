@@ -160,6 +160,7 @@ vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
   p.vbs = vbs;
   p.out = (uint16_t*)out;
   p.idx_width = topk;
+  p.seg_tiles = topk;
   p.table_cap = topk;
   p.lse = lse;
   return launch_attn(p, false, s) == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH;
@@ -254,14 +255,28 @@ extern "C" vsa_status vsa_preprocess(const void* k, const void* v, const int32_t
   return VSA_OK;
 }
 
-extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
-                                    const int32_t* sel_idx, const int32_t* vbs,
-                                    const void* kmean, const void* vsum, void* out,
-                                    int32_t batch, int32_t seq_len, int32_t prefix_len,
-                                    int32_t num_heads, int32_t head_dim, int32_t max_sel,
-                                    float sm_scale, void* workspace, size_t workspace_bytes,
-                                    vsa_stream_t stream) {
-  if (!q || !k || !v || !sel_idx || !vbs || !kmean || !vsum || !out) return VSA_ERR_NULL;
+namespace {
+
+// How a proxy call names the exactly computed video blocks of each query block.
+struct Selection {
+  int format;               // 0 padded rows, 1 bitmask, 2 BSR
+  const int32_t* idx;       // padded rows [B, H, Nv, max_sel], -1 = empty slot
+  const uint32_t* mask;     // bitmask rows [B, H, Nv, ceil(Nv/32)]
+  const int32_t* indptr;    // BSR row pointers [B*H*Nv + 1]
+  const int32_t* indices;   // BSR video-relative block ids
+  int nnz;                  // BSR: entries in indices
+  int max_sel;              // padded width, or the expected selection size
+};
+
+vsa_status proxy_call(const void* q, const void* k, const void* v, const Selection& sel,
+                      const int32_t* vbs, const void* kmean, const void* vsum, void* out,
+                      int32_t batch, int32_t seq_len, int32_t prefix_len, int32_t num_heads,
+                      int32_t head_dim, float sm_scale, void* workspace, size_t workspace_bytes,
+                      vsa_stream_t stream) {
+  const bool have_sel = sel.format == 0 ? sel.idx != nullptr
+                        : sel.format == 1 ? sel.mask != nullptr
+                                          : (sel.indptr != nullptr && sel.indices != nullptr);
+  if (!q || !k || !v || !have_sel || !vbs || !kmean || !vsum || !out) return VSA_ERR_NULL;
   vsa_status st = check_common(batch, seq_len, num_heads, head_dim);
   if (st != VSA_OK) return st;
   if (prefix_len <= 0 || prefix_len >= seq_len || prefix_len % kBlock != 0) return VSA_ERR_SHAPE;
@@ -269,14 +284,21 @@ extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
   const int nprefix = prefix_len / kBlock;
   const int nvideo = nblk - nprefix;
   const int nproxy = (nvideo + kBlock - 1) / kBlock;
+  const int max_sel = sel.max_sel;
   if (max_sel < 1 || max_sel > nvideo) return VSA_ERR_SHAPE;
-  const int table_cap = (nblk > nprefix + max_sel + nproxy) ? nblk : nprefix + max_sel + nproxy;
-  const size_t dyn = (size_t)table_cap * 12 + (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
+  if (sel.format == 2 && sel.nnz < 0) return VSA_ERR_SHAPE;
+  // rows of a bitmask or BSR selection may hold up to nvideo blocks
+  const int row_cap = sel.format == 0 ? max_sel : nvideo;
+  const int table_cap = (nblk > nprefix + row_cap + nproxy) ? nblk : nprefix + row_cap + nproxy;
+  const int words = (nvideo + 31) / 32;
+  size_t dyn = (size_t)table_cap * 12 + (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
+  if (sel.format == 1) dyn += (size_t)nvideo * 4 + (size_t)(words + 1) * 4;
   if (dyn > kMaxDynLds) return VSA_ERR_SHAPE;
   if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
   if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||
-      !is_aligned(kmean, 16) || !is_aligned(vsum, 16) || !is_aligned(sel_idx, 4) ||
-      !is_aligned(vbs, 4))
+      !is_aligned(kmean, 16) || !is_aligned(vsum, 16) || !is_aligned(vbs, 4) ||
+      (sel.idx && !is_aligned(sel.idx, 4)) || (sel.mask && !is_aligned(sel.mask, 4)) ||
+      (sel.indptr && !is_aligned(sel.indptr, 4)) || (sel.indices && !is_aligned(sel.indices, 4)))
     return VSA_ERR_ALIGN;
   const WsLayout ws = ws_layout(batch, num_heads, nblk, nproxy);
   if (!workspace || workspace_bytes < ws.total) return VSA_ERR_WORKSPACE;
@@ -313,16 +335,74 @@ extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
   p.vt_flags = wsb + ws.vf;
   p.pt = wsb + ws.pt;
   p.pt_flags = wsb + ws.pf;
-  p.idx = sel_idx;
+  p.idx = sel.idx;
+  p.sel_format = sel.format;
+  p.sel_mask = sel.mask;
+  p.sel_words = words;
+  p.sel_indptr = sel.indptr;
+  p.sel_indices = sel.indices;
+  p.sel_nnz = sel.nnz;
   p.vbs = vbs;
   p.out = (uint16_t*)out;
   p.idx_width = max_sel;
+  p.seg_tiles = nprefix + max_sel + nproxy;
   p.nprefix = nprefix;
   p.nvideo = nvideo;
   p.nproxy = nproxy;
   p.table_cap = table_cap;
   if (launch_attn(p, true, s) != hipSuccess) return VSA_ERR_LAUNCH;
   return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
+                                    const int32_t* sel_idx, const int32_t* vbs,
+                                    const void* kmean, const void* vsum, void* out,
+                                    int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                    int32_t num_heads, int32_t head_dim, int32_t max_sel,
+                                    float sm_scale, void* workspace, size_t workspace_bytes,
+                                    vsa_stream_t stream) {
+  Selection sel = {};
+  sel.format = 0;
+  sel.idx = sel_idx;
+  sel.max_sel = max_sel;
+  return proxy_call(q, k, v, sel, vbs, kmean, vsum, out, batch, seq_len, prefix_len, num_heads,
+                    head_dim, sm_scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" vsa_status vsa_fwd_proxy_bitmask(const void* q, const void* k, const void* v,
+                                            const uint32_t* sel_mask, const int32_t* vbs,
+                                            const void* kmean, const void* vsum, void* out,
+                                            int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                            int32_t num_heads, int32_t head_dim,
+                                            int32_t expected_sel, float sm_scale,
+                                            void* workspace, size_t workspace_bytes,
+                                            vsa_stream_t stream) {
+  Selection sel = {};
+  sel.format = 1;
+  sel.mask = sel_mask;
+  sel.max_sel = expected_sel;
+  return proxy_call(q, k, v, sel, vbs, kmean, vsum, out, batch, seq_len, prefix_len, num_heads,
+                    head_dim, sm_scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" vsa_status vsa_fwd_proxy_bsr(const void* q, const void* k, const void* v,
+                                        const int32_t* sel_indptr, const int32_t* sel_indices,
+                                        int32_t nnz, const int32_t* vbs, const void* kmean,
+                                        const void* vsum,
+                                        void* out, int32_t batch, int32_t seq_len,
+                                        int32_t prefix_len, int32_t num_heads, int32_t head_dim,
+                                        int32_t expected_sel, float sm_scale, void* workspace,
+                                        size_t workspace_bytes, vsa_stream_t stream) {
+  Selection sel = {};
+  sel.format = 2;
+  sel.indptr = sel_indptr;
+  sel.indices = sel_indices;
+  sel.nnz = nnz;
+  sel.max_sel = expected_sel;
+  return proxy_call(q, k, v, sel, vbs, kmean, vsum, out, batch, seq_len, prefix_len, num_heads,
+                    head_dim, sm_scale, workspace, workspace_bytes, stream);
 }
 
 namespace {

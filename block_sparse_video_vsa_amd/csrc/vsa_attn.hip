@@ -536,8 +536,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // (cell, block position in the sweep).
   const bool prefix_item = kProxy && qb < p.nprefix;
   const bool video_item = kProxy && !prefix_item;
-  const int ncand = !kProxy ? p.idx_width
-                            : (prefix_item ? p.nblk : p.nprefix + p.idx_width + p.nproxy);
   int* tab = sDyn;                       // [table_cap] entries
   int* ord = tab + p.table_cap;          // [table_cap] entries, processing order
   int* key = ord + p.table_cap;          // [table_cap] sort keys
@@ -545,19 +543,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float* wt = off + (kProxy ? p.nproxy * kBlock : 0);
   unsigned* bits = (unsigned*)(wt + (kProxy ? p.nproxy * kBlock : 0));
   const int64_t bh_tiles = (int64_t)bh * p.nblk;
+  // The index row: plain items and padded proxy rows read it in place; a BSR
+  // row is a slice of the index list; a bitmask row is first expanded in LDS
+  // into its set video blocks, ascending (bits past the last video block are
+  // ignored).
   const int32_t* row = p.idx + (kProxy ? ((int64_t)bh * p.nvideo + (qb - p.nprefix)) * p.idx_width
                                        : (int64_t)item * p.idx_width);
+  int width = p.idx_width;
+  if (kProxy && video_item && p.sel_format != 0) {
+    const int64_t rid = (int64_t)bh * p.nvideo + (qb - p.nprefix);
+    if (p.sel_format == 2) {
+      // row pointers are clamped to the index list, so malformed ones read
+      // nothing outside it
+      const int beg = min(max(p.sel_indptr[rid], 0), p.sel_nnz);
+      const int end = min(max(p.sel_indptr[rid + 1], beg), p.sel_nnz);
+      width = min(end - beg, p.nvideo);
+      row = p.sel_indices + beg;
+    } else {
+      int* list = (int*)(bits + p.nproxy * 2);   // [nvideo] expanded row
+      int* wpos = list + p.nvideo;               // [sel_words + 1] first list position per word
+      const uint32_t* mrow = p.sel_mask + rid * p.sel_words;
+      auto word = [&](int wi) {
+        const uint32_t m = mrow[wi];
+        const int valid = p.nvideo - 32 * wi;   // bits of this word that name a video block
+        return valid >= 32 ? m : (m & ((1u << valid) - 1u));
+      };
+      if (tid == 0) {
+        int acc = 0;
+        for (int wi = 0; wi < p.sel_words; ++wi) {
+          wpos[wi] = acc;
+          acc += __builtin_popcount(word(wi));
+        }
+        wpos[p.sel_words] = acc;
+      }
+      wg_barrier();
+      for (int wi = tid; wi < p.sel_words; wi += kThreads) {
+        uint32_t m = word(wi);
+        int pos = wpos[wi];
+        while (m) {
+          list[pos++] = 32 * wi + __builtin_ctz(m);
+          m &= m - 1u;
+        }
+      }
+      width = __builtin_amdgcn_readfirstlane(wpos[p.sel_words]);
+      wg_barrier();
+      row = list;
+    }
+  }
+  const int ncand = !kProxy ? p.idx_width : (prefix_item ? p.nblk : p.nprefix + width + p.nproxy);
   auto candidate = [&](int t) -> int {   // entry of candidate t, or -1
     int blk;
     if (!kProxy) {
       blk = row[t];
     } else if (prefix_item || t < p.nprefix) {
       blk = t;
-    } else if (t < p.nprefix + p.idx_width) {
+    } else if (t < p.nprefix + width) {
       const int s = row[t - p.nprefix];
       blk = (s >= 0 && s < p.nvideo) ? p.nprefix + s : -1;
     } else {
-      const int pt = t - p.nprefix - p.idx_width;
+      const int pt = t - p.nprefix - width;
       const int rows = min(p.nvideo - kBlock * pt, kBlock);
       return pt | (rows << kEntNvShift) | kEntProxy |
              (p.pt_flags[(int64_t)bh * p.nproxy + pt] ? kEntBf16 : 0);
@@ -572,8 +616,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
   if (tid == 0) {
     if (p.deterministic) {
-      // Start block from the dispatch slot: resident workgroups spread evenly.
-      sStart = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / p.sweep_slots) % p.nblk);
+      // Start block from the dispatch slot (a fixed 128 slots per XCD, so the
+      // order depends on nothing but the shapes): resident workgroups spread
+      // over the blocks.
+      sStart = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
     } else {
       // Start block: the average position of the XCD's resident workgroups.
       const unsigned long long prog =
@@ -628,7 +674,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int nbits = (p.nproxy * kBlock) / 32;
     for (int t = tid; t < nbits; t += kThreads) bits[t] = 0u;
     wg_barrier();
-    for (int t = tid; t < p.idx_width; t += kThreads) {
+    for (int t = tid; t < width; t += kThreads) {
       const int s = row[t];
       if (s >= 0 && s < p.nvideo) atomicOr(&bits[s >> 5], 1u << (s & 31));
     }
@@ -738,6 +784,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
   size_t dyn = (size_t)p.table_cap * 4 * 3;
   if (proxy) dyn += (size_t)p.nproxy * kBlock * 8 + (size_t)p.nproxy * 2 * 4;
+  if (proxy && p.sel_format == 1) dyn += (size_t)p.nvideo * 4 + (size_t)(p.sel_words + 1) * 4;
   return dyn;
 }
 
@@ -773,7 +820,7 @@ hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream)
   const size_t dyn = attn_dyn_lds(p, proxy);
   p.sweep_slots = resident_per_xcd(proxy, dyn);
   // about ten tiles of a typical item per sweep segment
-  const int tiles = p.idx_width + (proxy ? p.nprefix + p.nproxy : 0);
+  const int tiles = p.seg_tiles;
   p.nseg = std::min(kMaxSeg, std::max(1, (tiles + 5) / 10));
   const unsigned grid = (unsigned)p.items_per_xcd * 8u;
   if (proxy)

@@ -45,7 +45,13 @@ struct AttnParams {
   uint16_t* out;
   float* lse;               // optional [B, H, S] row log-sum-exp (nullptr: none)
   int batch, seq, heads, nblk;
-  int idx_width;            // topk or max_sel
+  int idx_width;            // topk or max_sel (padded rows)
+  int sel_format;           // proxy: 0 padded rows (idx), 1 bitmask, 2 BSR
+  const uint32_t* sel_mask; // bitmask rows [B*H*nvideo][sel_words]
+  int sel_words;
+  const int32_t* sel_indptr;   // BSR row pointers [B*H*nvideo + 1]
+  const int32_t* sel_indices;  // BSR video-relative block ids
+  int sel_nnz;              // BSR: entries in sel_indices
   int nprefix;              // prefix blocks (proxy mode)
   int nvideo;               // video blocks (proxy mode)
   int nproxy;               // proxy tiles of 64 video blocks (proxy mode)
@@ -54,6 +60,7 @@ struct AttnParams {
   int table_cap;            // tile-table capacity (entries)
   int sweep_slots;          // workgroups resident per XCD at once
   int nseg;                 // sweep segments per item (1..kMaxSeg)
+  int seg_tiles;            // tiles of a typical item (sizes the segments)
   int deterministic;        // 1: sweep start from the workgroup index only
   float c;                  // sm_scale * log2(e)
 };

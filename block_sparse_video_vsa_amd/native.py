@@ -54,6 +54,14 @@ _SIGNATURES = {
                                    _c_void_p, _size_t, _c_void_p]),
     "vsa_merge": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _i32, _i32, _i32, _i32, _c_void_p]),
+    "vsa_fwd_proxy_bitmask": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _f32, _c_void_p, _size_t,
+                                             _c_void_p]),
+    "vsa_fwd_proxy_bsr": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t,
+                                         _c_void_p]),
     "vsa_cube_count": (_size_t, [_i32, _i32, _i32]),
     "vsa_cube_vbs": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _size_t]),
     "vsa_tile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -373,3 +381,57 @@ def vsa_merge(o1, lse1, o2, lse2, out=None, lse_out=None):
                        B, S, H, D, _stream(dev))
     _check("vsa_merge", st)
     return out, lse_out
+
+
+def _proxy_common(q, k, v, vbs, kmean, vsum, out):
+    dev = q.device
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev, (B, S, H, D))
+    nblk = S // BLOCK
+    _need(vbs, "vbs", torch.int32, dev, (nblk,))
+    _need(kmean, "kmean", torch.bfloat16, dev, (B, nblk, H, D))
+    _need(vsum, "vsum", torch.bfloat16, dev, (B, nblk, H, D))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev, (B, S, H, D))
+    return dev, B, S, H, D, out
+
+
+def vsa_fwd_proxy_bitmask(q, k, v, sel_mask, vbs, kmean, vsum, prefix_len, expected_sel,
+                          sm_scale=None, out=None, workspace=None):
+    """Proxy forward with a bitmask selection (C ABI vsa_fwd_proxy_bitmask).
+
+    sel_mask: int32 or uint32-valued tensor [B, H, Nv, ceil(Nv/32)] (int32 storage)."""
+    lib = load_library()
+    dev, B, S, H, D, out = _proxy_common(q, k, v, vbs, kmean, vsum, out)
+    nv = (S - prefix_len) // BLOCK
+    _need(sel_mask, "sel_mask", torch.int32, dev, (B, H, nv, (nv + 31) // 32))
+    nbytes = proxy_workspace_size(B, S, prefix_len, H, D)
+    if workspace is None:
+        workspace = _workspace(dev, max(nbytes, 1))
+    st = lib.vsa_fwd_proxy_bitmask(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_mask), _ptr(vbs), _ptr(kmean),
+                                   _ptr(vsum), _ptr(out), B, S, prefix_len, H, D, int(expected_sel),
+                                   _default_scale(sm_scale), _ptr(workspace), workspace.numel(),
+                                   _stream(dev))
+    _check("vsa_fwd_proxy_bitmask", st)
+    return out
+
+
+def vsa_fwd_proxy_bsr(q, k, v, sel_indptr, sel_indices, vbs, kmean, vsum, prefix_len, expected_sel,
+                      sm_scale=None, out=None, workspace=None):
+    """Proxy forward with a BSR selection (C ABI vsa_fwd_proxy_bsr)."""
+    lib = load_library()
+    dev, B, S, H, D, out = _proxy_common(q, k, v, vbs, kmean, vsum, out)
+    nv = (S - prefix_len) // BLOCK
+    _need(sel_indptr, "sel_indptr", torch.int32, dev, (B * H * nv + 1,))
+    _need(sel_indices, "sel_indices", torch.int32, dev)
+    nbytes = proxy_workspace_size(B, S, prefix_len, H, D)
+    if workspace is None:
+        workspace = _workspace(dev, max(nbytes, 1))
+    st = lib.vsa_fwd_proxy_bsr(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_indptr), _ptr(sel_indices),
+                               int(sel_indices.numel()), _ptr(vbs), _ptr(kmean), _ptr(vsum), _ptr(out),
+                               B, S, prefix_len, H, D, int(expected_sel), _default_scale(sm_scale),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("vsa_fwd_proxy_bsr", st)
+    return out

@@ -331,3 +331,28 @@ def effective_flops_proxy(sel_idx: np.ndarray, vbs: np.ndarray, n_prefix_blocks:
     n_proxy = (vv > 0).sum() - n_sel_nonzero
     proxy = (n_proxy * vv[None, None, :]).sum()
     return float(4 * head_dim * exact), float(4 * head_dim * proxy)
+
+
+# --------------------------------------------------------------------------
+# selection formats (same selection, other encodings)
+# --------------------------------------------------------------------------
+def sel_to_bitmask(sel_idx: np.ndarray, nvideo: int) -> np.ndarray:
+    """Padded rows [..., width] (-1 = empty) -> packed words [..., ceil(nvideo/32)] (uint32 bits
+    in int32 storage): bit c % 32 of word c // 32 is set for each listed video block c."""
+    rows = sel_idx.reshape(-1, sel_idx.shape[-1])
+    nw = (nvideo + 31) // 32
+    out = np.zeros((rows.shape[0], nw), dtype=np.uint32)
+    for r in range(rows.shape[0]):
+        for c in rows[r]:
+            if 0 <= c < nvideo:
+                out[r, c // 32] |= np.uint32(1) << np.uint32(c % 32)
+    return out.view(np.int32).reshape(sel_idx.shape[:-1] + (nw,))
+
+
+def sel_to_bsr(sel_idx: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Padded rows -> (indptr [rows + 1], indices) over the rows in C order, -1 entries dropped."""
+    rows = sel_idx.reshape(-1, sel_idx.shape[-1])
+    keep = rows >= 0
+    counts = keep.sum(axis=1)
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return indptr, rows[keep].astype(np.int32)

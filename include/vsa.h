@@ -183,6 +183,42 @@ vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
                          vsa_stream_t stream);
 
 /*
+ * The same proxy forward with the exact blocks named in the two formats of
+ * [PX] (FlashInfer description, "Bitmask format"); both give bit-identical
+ * results to vsa_fwd_proxy with the same selection in deterministic mode.
+ *
+ *   sel_mask      uint32 [batch, num_heads, nvideo, ceil(nvideo/32)], one row of
+ *                 words per (batch, head, video query block): bit (c % 32) of
+ *                 word c / 32 selects video block c; bits past the last video
+ *                 block in the final word are ignored.
+ *   sel_indptr    int32 [batch * num_heads * nvideo + 1], non-decreasing, row
+ *                 pointers into sel_indices for the rows in (batch, head, video
+ *                 block) order; sel_indices int32 [nnz], video-relative block
+ *                 ids (distinct per row; -1 or out-of-range entries are
+ *                 skipped).  Row pointers are clamped to [0, nnz] on the device,
+ *                 so a malformed list reads nothing outside sel_indices.
+ *   expected_sel  the typical number of selected blocks per row, 1..nvideo: it
+ *                 only sizes the sweep segments (rows may hold more or fewer);
+ *                 pass the max_sel of a padded call to reproduce its order.
+ *   other arguments, outputs and errors as vsa_fwd_proxy (a row may select up
+ *   to every video block, which these calls size their LDS tables for).
+ */
+vsa_status vsa_fwd_proxy_bitmask(const void* q, const void* k, const void* v,
+                                 const uint32_t* sel_mask, const int32_t* vbs,
+                                 const void* kmean, const void* vsum, void* out,
+                                 int32_t batch, int32_t seq_len, int32_t prefix_len,
+                                 int32_t num_heads, int32_t head_dim, int32_t expected_sel,
+                                 float sm_scale, void* workspace, size_t workspace_bytes,
+                                 vsa_stream_t stream);
+vsa_status vsa_fwd_proxy_bsr(const void* q, const void* k, const void* v,
+                             const int32_t* sel_indptr, const int32_t* sel_indices, int32_t nnz,
+                             const int32_t* vbs, const void* kmean, const void* vsum, void* out,
+                             int32_t batch, int32_t seq_len, int32_t prefix_len,
+                             int32_t num_heads, int32_t head_dim, int32_t expected_sel,
+                             float sm_scale, void* workspace, size_t workspace_bytes,
+                             vsa_stream_t stream);
+
+/*
  * vsa_fwd_lse -- vsa_fwd that also returns the row statistics.
  *
  *   lse           float32 [batch, num_heads, seq_len] output, 4-byte aligned:

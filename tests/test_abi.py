@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported(lib):
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
             "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
-            "vsa_merge"} <= set(names)
+            "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -167,3 +167,33 @@ def test_lse_and_merge_reject_bad_arguments_on_host(lib):
     assert m(S=0) == SHAPE
     assert m(o1=FAKE + 8) == ALIGN
     assert m(l1=FAKE + 2) == ALIGN
+
+
+def test_bitmask_and_bsr_proxy_reject_bad_arguments_on_host(lib):
+    S, P = 64 * 40, 128                        # 38 video blocks
+    bm = lambda mask=FAKE, es=5: lib.vsa_fwd_proxy_bitmask(FAKE, FAKE, FAKE, mask, FAKE, FAKE, FAKE, FAKE,
+                                                         1, S, P, 2, 128, es, 0.088, FAKE, 1 << 30, None)
+    assert bm(mask=None) == NULL
+    assert bm(es=0) == SHAPE
+    assert bm(es=39) == SHAPE
+    assert bm(mask=FAKE + 2) == ALIGN
+    bs = lambda ip=FAKE, ix=FAKE, nnz=10: lib.vsa_fwd_proxy_bsr(FAKE, FAKE, FAKE, ip, ix, nnz, FAKE, FAKE,
+                                                               FAKE, FAKE, 1, S, P, 2, 128, 5, 0.088,
+                                                               FAKE, 1 << 30, None)
+    assert bs(ip=None) == NULL
+    assert bs(ix=None) == NULL
+    assert bs(nnz=-1) == SHAPE
+    assert bs(ix=FAKE + 1) == ALIGN
+
+
+def test_selection_format_helpers():
+    import numpy as np
+    from block_sparse_video_vsa_amd import workloads as W
+    sel = np.array([[[[3, 0, -1, 37], [-1, -1, -1, -1], [5, 31, 32, 33]]]], np.int32)
+    m = W.sel_to_bitmask(sel, 38).view(np.uint32)
+    assert m.shape == (1, 1, 3, 2)
+    assert m[0, 0, 0].tolist() == [(1 << 3) | 1, 1 << 5]
+    assert m[0, 0, 1].tolist() == [0, 0]
+    assert m[0, 0, 2].tolist() == [(1 << 5) | (1 << 31), 0b11]
+    ip, ix = W.sel_to_bsr(sel)
+    assert ip.tolist() == [0, 3, 3, 7] and ix.tolist() == [3, 0, 37, 5, 31, 32, 33]

@@ -475,3 +475,59 @@ def test_merge_against_the_oracle(dev):
     assert np.array_equal(np.isfinite(lo), fin) and np.all(np.isneginf(lo[~fin]))
     assert np.all(np.abs(lo[fin] - lm[fin]) <= 1e-5 * (1 + np.abs(lm[fin])))
     assert not got[:, 5:10].any()                      # both parts empty -> zeros
+
+
+# --------------------------------------------------------------------------
+# bitmask and BSR selections for the proxy forward
+# --------------------------------------------------------------------------
+def _proxy_formats(dev, wl_q, wl_k, wl_v, sel, vbs, prefix_len, scale, garbage_bits=False):
+    """Outputs of the padded, bitmask and BSR calls (deterministic mode)."""
+    nv = sel.shape[2]
+    width = sel.shape[-1]
+    dq, dk, dv, dvbs = (to_dev(wl_q, dev, True), to_dev(wl_k, dev, True), to_dev(wl_v, dev, True),
+                        to_dev(vbs, dev))
+    km, vs = vsa.vsa_preprocess(dk, dv, dvbs)
+    mask = W.sel_to_bitmask(sel, nv)
+    if garbage_bits and nv % 32:
+        mask = mask.view(np.uint32).copy()
+        mask[..., -1] |= np.uint32(0xFFFFFFFF) << np.uint32(nv % 32)   # bits past the last block
+        mask = mask.view(np.int32)
+    indptr, indices = W.sel_to_bsr(sel)
+    with vsa.deterministic():
+        a = vsa.vsa_fwd_proxy(dq, dk, dv, to_dev(sel, dev), dvbs, km, vs, prefix_len, scale)
+        b = vsa.vsa_fwd_proxy_bitmask(dq, dk, dv, to_dev(mask, dev), dvbs, km, vs, prefix_len, width, scale)
+        c = vsa.vsa_fwd_proxy_bsr(dq, dk, dv, to_dev(indptr, dev), to_dev(indices, dev), dvbs, km, vs,
+                                  prefix_len, width, scale)
+    torch.cuda.synchronize()
+    return from_dev(a), from_dev(b), from_dev(c)
+
+
+def test_proxy_bitmask_and_bsr_small_bitwise(dev):
+    """Same selection in three encodings: bit-identical outputs, and the oracle bar."""
+    rng = np.random.default_rng(70)
+    H = 3
+    vbs = np.array([64, 64] + [64, 12, 0, 64, 33, 64, 1, 64, 50, 64, 64, 64] * 6, np.int32)
+    npb = 2
+    nv = vbs.size - npb                       # 72 video blocks: the last word is partial
+    S = 64 * vbs.size
+    q, k, v = (_rand_bf16(rng, (1, S, H, D)) for _ in range(3))
+    width = 9
+    sel = np.full((1, H, nv, width), -1, np.int32)
+    for h in range(H):
+        for c in range(nv):
+            picks = rng.choice(nv, size=int(rng.integers(0, width + 1)), replace=False)
+            sel[0, h, c, :picks.size] = picks
+    a, b, c = _proxy_formats(dev, q, k, v, sel, vbs, 64 * npb, float(1 / math.sqrt(D)), True)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    km_o, vs_o = O.vsa_preprocess(k, v, vbs)
+    o64 = O.vsa_fwd_proxy(q, k, v, sel, vbs, km_o, vs_o, 64 * npb, np.float32(1 / math.sqrt(D)))
+    g = grade_full(b, o64, vbs)
+    assert g.ok(), str(g)
+
+
+def test_proxy_bitmask_and_bsr_config4_bitwise(dev):
+    wl = W.generate("4")
+    a, b, c = _proxy_formats(dev, wl.q, wl.k, wl.v, wl.sel_idx, wl.vbs, wl.config.prefix_len,
+                             float(wl.sm_scale), True)
+    assert np.array_equal(a, b), "bitmask differs from the padded selection"
+    assert np.array_equal(a, c), "BSR differs from the padded selection"
