@@ -41,7 +41,8 @@ BLOCK = 64
 
 __all__ = ["bf16_to_f64", "f64_to_bf16", "vsa_fwd", "vsa_fwd_item", "vsa_preprocess",
            "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots", "cube_layout", "cube_tile",
-           "cube_untile", "vsa_fwd_lse_item", "vsa_fwd_lse", "merge_partials"]
+           "cube_untile", "vsa_fwd_lse_item", "vsa_fwd_lse", "merge_partials", "block_scores",
+           "route_topk"]
 
 
 # --------------------------------------------------------------------------
@@ -351,3 +352,46 @@ def merge_partials(o1, lse1, o2, lse2):
     den = np.where(empty, 1.0, tot)[..., None]
     o = (w1[..., None] * o1 + w2[..., None] * o2) / den
     return np.where(empty[..., None], 0.0, o), lse
+
+
+# --------------------------------------------------------------------------
+# routing: top-k key blocks by block-mean scores
+# --------------------------------------------------------------------------
+def block_scores(qmean, kmean, b: int, h: int):
+    """Score matrix [nq, nk] of one (batch, head): s[i, j] = sum_d qmean_i[d] * kmean_j[d].
+
+    The bf16 inputs are widened exactly; each product of two bf16 values is
+    exact in float64, and the 128 products are added in order d = 0, 1, ...,
+    one rounding per addition, which fixes every score to the last bit (a
+    fused multiply-add per term gives the same sequence of values).
+    """
+    qm = bf16_to_f64(qmean[b, :, h, :])
+    km = bf16_to_f64(kmean[b, :, h, :])
+    s = np.zeros((qm.shape[0], km.shape[0]))
+    for d in range(qm.shape[1]):
+        s = s + np.multiply.outer(qm[:, d], km[:, d])
+    return s
+
+
+def route_topk(qmean, kmean, vbs, topk: int):
+    """topk_idx [B, H, nq, topk]: per query block, the topk key blocks of highest score.
+
+    Blocks with vbs = 0 hold no keys and are never chosen; ties go to the lower
+    block index; each row lists its blocks by descending score.  Rows with
+    fewer than topk eligible blocks are padded with -1.
+    """
+    qmean = np.asarray(qmean)
+    B, nq, H, _ = qmean.shape
+    vbs = np.asarray(vbs)
+    eligible = vbs[:kmean.shape[1]] > 0
+    out = np.full((B, H, nq, topk), -1, dtype=np.int32)
+    idx = np.arange(kmean.shape[1])
+    for b in range(B):
+        for h in range(H):
+            s = block_scores(qmean, kmean, b, h)
+            for i in range(nq):
+                cand = idx[eligible]
+                order = np.lexsort((cand, -s[i, cand]))     # descending score, then lower index
+                pick = cand[order[:topk]]
+                out[b, h, i, :pick.size] = pick
+    return out

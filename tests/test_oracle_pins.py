@@ -468,3 +468,50 @@ def test_merge_with_an_empty_part_and_symmetry():
     m, lmid = O.merge_partials(o1, l1, o2, l1)
     assert np.allclose(m, (o1 + o2) / 2, rtol=1e-15, atol=1e-15)
     assert np.allclose(lmid, l1 + math.log(2.0), rtol=1e-15, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+def test_block_scores_are_exact_for_small_integer_data():
+    """Integer-valued bf16 means: every partial sum is an exact integer, so the
+    ordered float64 sum equals the exact rational dot product."""
+    from fractions import Fraction
+    rng = np.random.default_rng(80)
+    qi = rng.integers(-50, 51, size=(1, 6, 1, 128))
+    ki = rng.integers(-50, 51, size=(1, 9, 1, 128))
+    qm = W.f32_to_bf16_bits(qi.astype(np.float32))
+    km = W.f32_to_bf16_bits(ki.astype(np.float32))
+    s = O.block_scores(qm, km, 0, 0)
+    for i in range(6):
+        for j in range(9):
+            exact = sum(Fraction(int(a)) * Fraction(int(c)) for a, c in zip(qi[0, i, 0], ki[0, j, 0]))
+            assert s[i, j] == float(exact)
+
+
+def test_route_topk_against_a_brute_force_sort_with_ties():
+    rng = np.random.default_rng(81)
+    nb, H, D = 12, 2, 128
+    k = rng.integers(-3, 4, size=(1, nb, H, D)).astype(np.float32)
+    k[0, 7] = k[0, 2]                     # blocks 2 and 7 tie for every query
+    k[0, 9] = k[0, 4]
+    q = rng.integers(-3, 4, size=(1, nb, H, D)).astype(np.float32)
+    qm, km = W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k)
+    vbs = np.full(nb, 64, np.int32)
+    vbs[5] = 0                            # an empty block is never chosen
+    got = O.route_topk(qm, km, vbs, 6)
+    for h in range(H):
+        for i in range(nb):
+            scores = [(-(float(np.dot(q[0, i, h].astype(np.float64), k[0, j, h].astype(np.float64)))), j)
+                      for j in range(nb) if vbs[j] > 0]
+            want = [j for _, j in sorted(scores)[:6]]
+            assert got[0, h, i].tolist() == want
+    assert not (got == 5).any()
+
+
+def test_route_topk_pads_when_few_blocks_are_eligible():
+    qm = W.f32_to_bf16_bits(np.ones((1, 4, 1, 128), np.float32))
+    km = W.f32_to_bf16_bits(np.arange(4, dtype=np.float32)[None, :, None, None] * np.ones((1, 4, 1, 128), np.float32))
+    vbs = np.array([64, 0, 64, 0], np.int32)
+    got = O.route_topk(qm, km, vbs, 3)
+    assert got[0, 0, 0].tolist() == [2, 0, -1]
