@@ -312,6 +312,68 @@ def bench_merge(args, cfg, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_route(args, cfg, dev):
+    """Routing step on the config's shapes: block means of q and k, then top-k by score."""
+    import torch
+
+    import block_sparse_video_vsa_amd as vsa
+    from block_sparse_video_vsa_amd import workloads as W
+
+    wl = W.generate(cfg)
+    B, S, H, D = wl.q.shape
+    nb = S // 64
+    topk = int(wl.topk_idx.shape[-1])
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k = up(wl.q), up(wl.k)
+    vbs = torch.from_numpy(wl.vbs).to(dev)
+    qm = torch.empty((B, nb, H, D), dtype=torch.bfloat16, device=dev)
+    km, scratch = torch.empty_like(qm), torch.empty_like(qm)
+    idx = torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vsa.vsa_preprocess(q, q, vbs, qm, scratch)
+        vsa.vsa_preprocess(k, k, vbs, km, scratch)
+        if ev is not None:
+            ev[1].record(stream)
+        vsa.vsa_route_topk(qm, km, vbs, topk, out=idx)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    means_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    route_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flop = 2.0 * B * H * nb * nb * D            # float64 multiply-adds of the scores
+    rec = {
+        "metric": "routing (block means + top-k by block-mean score) ms/call",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": cfg.description, "batch": B, "heads": H, "blocks": nb, "topk": topk},
+        "kernels_ms": {"block_means_avg": round(means_ms, 4), "route_topk_avg": round(route_ms, 4)},
+        "roofline": {"bound": "alu", "achieved": round(flop / (route_ms * 1e-3) / 1e12, 3),
+                     "peak": 78.6, "unit": "TFLOP/s",
+                     "frac": round(flop / (route_ms * 1e-3) / 1e12 / 78.6, 4), "traffic": None,
+                     "note": "score multiply-adds only (float64 vector peak); the ranking adds "
+                             "about 2 * blocks comparisons per score"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,7 +382,7 @@ def main():
     ap.add_argument("--config", default="2")
     ap.add_argument("--sel-format", default="padded", choices=["padded", "bitmask", "bsr"],
                     help="proxy workload: encoding of the exact-block selection")
-    ap.add_argument("--op", default="attention", choices=["attention", "tile", "merge"],
+    ap.add_argument("--op", default="attention", choices=["attention", "tile", "merge", "route"],
                     help="tile: the cube tile/untile layout kernels on the config's grid; "
                          "merge: the merge of two partial results at the config's shape")
     ap.add_argument("--cpu-items", type=int, default=4000)
@@ -360,6 +422,9 @@ def main():
         return
     if args.op == "merge":
         bench_merge(args, cfg, dev)
+        return
+    if args.op == "route":
+        bench_route(args, cfg, dev)
         return
     if cfg.proxy:
         bench_proxy(args, cfg, dev)

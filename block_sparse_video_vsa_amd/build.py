@@ -7,7 +7,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/vsa_pack.hip", "csrc/vsa_attn.hip", "csrc/vsa_layout.hip", "csrc/vsa_merge.hip", "csrc/vsa_api.hip"]
+SOURCES = ["csrc/vsa_pack.hip", "csrc/vsa_attn.hip", "csrc/vsa_layout.hip", "csrc/vsa_merge.hip", "csrc/vsa_route.hip",
+           "csrc/vsa_api.hip"]
 OUTPUT = os.path.join(HERE, "libvsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

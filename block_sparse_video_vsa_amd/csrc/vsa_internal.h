@@ -70,6 +70,11 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+// Routing: top-k key blocks by block-mean scores.
+int route_blocks_per_wg(int nblk);
+size_t route_lds_bytes(int nblk);
+hipError_t launch_route(const uint16_t* qmean, const uint16_t* kmean, const int32_t* vbs,
+                        int32_t* out, int batch, int nblk, int heads, int topk, hipStream_t stream);
 // Merge of two partial attention results over disjoint key sets.
 hipError_t launch_merge(const uint16_t* o1, const float* lse1, const uint16_t* o2, const float* lse2,
                         uint16_t* out, float* lse_out, int batch, int seq, int heads, int head_dim,

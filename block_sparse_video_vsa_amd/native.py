@@ -62,6 +62,8 @@ _SIGNATURES = {
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t,
                                          _c_void_p]),
+    "vsa_route_topk": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                      _i32, _i32, _c_void_p]),
     "vsa_cube_count": (_size_t, [_i32, _i32, _i32]),
     "vsa_cube_vbs": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _size_t]),
     "vsa_tile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -434,4 +436,20 @@ def vsa_fwd_proxy_bsr(q, k, v, sel_indptr, sel_indices, vbs, kmean, vsum, prefix
                                B, S, prefix_len, H, D, int(expected_sel), _default_scale(sm_scale),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _check("vsa_fwd_proxy_bsr", st)
+    return out
+
+
+def vsa_route_topk(qmean, kmean, vbs, topk: int, out=None):
+    """Top-k key blocks per query block by block-mean scores (C ABI vsa_route_topk)."""
+    lib = load_library()
+    dev = qmean.device
+    B, nb, H, D = qmean.shape
+    _need(qmean, "qmean", torch.bfloat16, dev)
+    _need(kmean, "kmean", torch.bfloat16, dev, (B, nb, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (nb,))
+    if out is None:
+        out = torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
+    _need(out, "topk_idx", torch.int32, dev, (B, H, nb, topk))
+    _check("vsa_route_topk", lib.vsa_route_topk(_ptr(qmean), _ptr(kmean), _ptr(vbs), _ptr(out), B, nb, H,
+                                                D, topk, _stream(dev)))
     return out

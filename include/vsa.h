@@ -257,6 +257,33 @@ vsa_status vsa_merge(const void* o1, const float* lse1, const void* o2, const fl
                      int32_t num_heads, int32_t head_dim, vsa_stream_t stream);
 
 /*
+ * vsa_route_topk -- exact-block selection by block-mean scores, the routing
+ * step before the attention.  [RUN] makes a video query block exact on the key
+ * blocks whose centroid score passes a per-block threshold it does not define;
+ * this call takes the topk highest scores instead.  For each (batch, head,
+ * query block) i the score of key block j is sum_d qmean[i, d] * kmean[j, d],
+ * accumulated in float64 in the order d = 0..127 (exact products, one rounding
+ * per term, so the result is fixed to the last bit); the topk eligible blocks
+ * of highest score are written by descending score, ties to the lower index.
+ * Blocks with vbs = 0 are not eligible; a row with fewer than topk eligible
+ * blocks is padded with -1.
+ *
+ *   qmean, kmean  bf16 [batch, num_blocks, num_heads, head_dim] block means
+ *                 (vsa_preprocess of q, resp. k, gives them).
+ *   vbs           int32 [num_blocks].
+ *   topk_idx      int32 [batch, num_heads, num_blocks, topk] output: ready to
+ *                 be the topk_idx of vsa_fwd.
+ *   num_blocks    1 .. 7680; head_dim must be 128; 1 <= topk <= num_blocks.
+ *
+ * Device memory, caller-owned, enqueued on `stream`; kmean must be 16-byte
+ * aligned, qmean 2-byte, vbs and topk_idx 4-byte (VSA_ERR_ALIGN otherwise).
+ */
+vsa_status vsa_route_topk(const void* qmean, const void* kmean, const int32_t* vbs,
+                          int32_t* topk_idx, int32_t batch, int32_t num_blocks,
+                          int32_t num_heads, int32_t head_dim, int32_t topk,
+                          vsa_stream_t stream);
+
+/*
  * Cube tiling of a latent video grid ([SH]: 4 x 4 x 4 cubes of 64 tokens,
  * padded to 64 * cubes rows).  The grid T x Hh x W has ceil(T/4) * ceil(Hh/4) *
  * ceil(W/4) cubes, numbered row-major over the cube grid; inside a cube the real

@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported(lib):
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
             "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
-            "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr"} <= set(names)
+            "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -197,3 +197,15 @@ def test_selection_format_helpers():
     assert m[0, 0, 2].tolist() == [(1 << 5) | (1 << 31), 0b11]
     ip, ix = W.sel_to_bsr(sel)
     assert ip.tolist() == [0, 3, 3, 7] and ix.tolist() == [3, 0, 37, 5, 31, 32, 33]
+
+
+def test_route_rejects_bad_arguments_on_host(lib):
+    r = lambda **kw: lib.vsa_route_topk(kw.get("q", FAKE), FAKE, FAKE, kw.get("o", FAKE), 1,
+                                        kw.get("nb", 624), 2, kw.get("D", 128), kw.get("k", 78), None)
+    assert r(q=None) == NULL
+    assert r(o=None) == NULL
+    assert r(D=64) == UNSUP
+    assert r(k=0) == SHAPE
+    assert r(k=625) == SHAPE
+    assert r(nb=7681, k=5) == SHAPE
+    assert r(q=FAKE + 1) == ALIGN

@@ -515,3 +515,18 @@ def test_route_topk_pads_when_few_blocks_are_eligible():
     vbs = np.array([64, 0, 64, 0], np.int32)
     got = O.route_topk(qm, km, vbs, 3)
     assert got[0, 0, 0].tolist() == [2, 0, -1]
+
+
+def test_block_scores_round_after_each_term_in_d_order():
+    """Scores are the d = 0..127 running sum in float64, one rounding per term:
+    2^60 + 1 - 2^60 gives 0 (the exact sum is 1), adding the 1 last gives 1,
+    and 1 + 2^-30 survives (a float32 accumulator would lose it)."""
+    q = np.zeros((1, 3, 1, 128), np.float32)
+    q[0, 0, 0, :3] = [2.0 ** 60, 1.0, -(2.0 ** 60)]
+    q[0, 1, 0, :3] = [2.0 ** 60, -(2.0 ** 60), 1.0]
+    q[0, 2, 0, :2] = [1.0, 2.0 ** -30]
+    k = np.ones((1, 1, 1, 128), np.float32)
+    s = O.block_scores(W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k), 0, 0)
+    assert s[0, 0] == 0.0
+    assert s[1, 0] == 1.0
+    assert s[2, 0] == 1.0 + 2.0 ** -30

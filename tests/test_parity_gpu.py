@@ -531,3 +531,72 @@ def test_proxy_bitmask_and_bsr_config4_bitwise(dev):
                              float(wl.sm_scale), True)
     assert np.array_equal(a, b), "bitmask differs from the padded selection"
     assert np.array_equal(a, c), "BSR differs from the padded selection"
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,topk,heads", [("0", 3, None), ("1", 11, None), ("2", 78, 3), ("3b", 180, 2)])
+def test_route_topk_bitwise(dev, name, topk, heads):
+    """Block means from q and k, then the top-k blocks: indices identical to the oracle's."""
+    wl = W.generate(name)
+    q, k = wl.q, wl.k
+    if heads is not None:            # large grids: a few heads keep the oracle quick
+        q, k = np.ascontiguousarray(q[:, :, :heads]), np.ascontiguousarray(k[:, :, :heads])
+    dq, dk, dvbs = to_dev(q, dev, True), to_dev(k, dev, True), to_dev(wl.vbs, dev)
+    qm, _ = vsa.vsa_preprocess(dq, dq, dvbs)
+    km, _ = vsa.vsa_preprocess(dk, dk, dvbs)
+    got = vsa.vsa_route_topk(qm, km, dvbs, topk)
+    torch.cuda.synchronize()
+    qm_o, _ = O.vsa_preprocess(q, q, wl.vbs)
+    km_o, _ = O.vsa_preprocess(k, k, wl.vbs)
+    assert np.array_equal(from_dev(qm), qm_o) and np.array_equal(from_dev(km), km_o)
+    want = O.route_topk(qm_o, km_o, wl.vbs, topk)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("nblk,heads,topks,kind", [
+    (200, 2, (1, 50, 200), "ties"),      # 8 query blocks per workgroup, ragged last group
+    (200, 1, (7, 200), "zeros"),         # every score equal: pure index order
+    (1000, 1, (1, 125), "ties"),         # 4 per workgroup
+    (2000, 1, (250,), "random"),         # 2 per workgroup
+    (3200, 1, (3, 400), "random"),       # 1 per workgroup
+])
+def test_route_topk_ties_and_empty_blocks(dev, nblk, heads, topks, kind):
+    """Synthetic block means with exact ties and empty blocks (vbs = 0): indices equal the oracle's."""
+    rng = np.random.default_rng(nblk * 7 + heads)
+    if kind == "zeros":
+        qm = np.zeros((1, nblk, heads, 128), np.float32)
+        km = np.zeros((1, nblk, heads, 128), np.float32)
+    else:
+        qm = rng.standard_normal((1, nblk, heads, 128)).astype(np.float32)
+        km = rng.standard_normal((1, nblk, heads, 128)).astype(np.float32)
+        if kind == "ties":               # key means drawn from 3 distinct rows: many equal scores
+            km = km[:, rng.integers(0, 3, nblk)]
+    qm_b, km_b = W.f32_to_bf16_bits(qm), W.f32_to_bf16_bits(km)
+    vbs = rng.integers(1, 65, nblk).astype(np.int32)
+    vbs[rng.random(nblk) < 0.1] = 0
+    dq, dk, dvbs = to_dev(qm_b, dev, True), to_dev(km_b, dev, True), to_dev(vbs, dev)
+    # a row's top t is the first t entries of its longest list: one oracle call
+    want = O.route_topk(qm_b, km_b, vbs, max(topks))
+    for topk in topks:
+        got = vsa.vsa_route_topk(dq, dk, dvbs, topk)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), want[..., :topk]), f"topk={topk}"
+
+
+def test_route_topk_follows_sequential_rounding(dev):
+    """Block 0 scores 2^60 + 1 - 2^60: 0 after rounding in d order (exactly it
+    would be 1); block 1 scores 0.5.  The kernel ranks by the rounded scores."""
+    qm = np.zeros((1, 2, 1, 128), np.float32)
+    qm[0, :, 0, :3] = [2.0 ** 60, 1.0, -(2.0 ** 60)]
+    km = np.zeros((1, 2, 1, 128), np.float32)
+    km[0, 0, 0, :3] = 1.0
+    km[0, 1, 0, 1] = 0.5
+    qm_b, km_b = W.f32_to_bf16_bits(qm), W.f32_to_bf16_bits(km)
+    vbs = np.array([64, 64], np.int32)
+    want = O.route_topk(qm_b, km_b, vbs, 2)
+    assert want[0, 0, 0].tolist() == [1, 0]
+    got = vsa.vsa_route_topk(to_dev(qm_b, dev, True), to_dev(km_b, dev, True), to_dev(vbs, dev), 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
