@@ -114,7 +114,7 @@ vsa_status check_fwd(const void* q, const void* k, const void* v, const int32_t*
   const int nblk = seq_len / kBlock;
   if (need_q) {
     if (topk < 1 || topk > nblk) return VSA_ERR_SHAPE;
-    if ((size_t)topk * 12 > kMaxDynLds) return VSA_ERR_SHAPE;
+    if ((size_t)topk * 8 > kMaxDynLds) return VSA_ERR_SHAPE;   // 8 bytes of tile table per entry
     if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
     if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(out, 16) ||
         !is_aligned(topk_idx, 4))
@@ -292,8 +292,12 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
   const int row_cap = sel.format == 0 ? max_sel : nvideo;
   const int table_cap = (nblk > nprefix + row_cap + nproxy) ? nblk : nprefix + row_cap + nproxy;
   const int words = (nvideo + 31) / 32;
-  size_t dyn = (size_t)table_cap * 12 + (size_t)nproxy * kBlock * 8 + (size_t)nproxy * 8;
-  if (sel.format == 1) dyn += (size_t)nvideo * 4 + (size_t)(words + 1) * 4;
+  // tile table of 8 bytes per entry; video items add a byte of weight per
+  // video block and the selected-block bits
+  const size_t table = (size_t)table_cap * 8;
+  const size_t video = (size_t)(nprefix + row_cap + nproxy) * 8 + (size_t)nproxy * kBlock +
+                       (size_t)nproxy * 8;
+  const size_t dyn = table > video ? table : video;
   if (dyn > kMaxDynLds) return VSA_ERR_SHAPE;
   if (!isfinite(sm_scale) || sm_scale < 0.0f) return VSA_ERR_VALUE;
   if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||

@@ -244,18 +244,27 @@ struct State {
   float lsum;              // this lane's share of the softmax denominator
 };
 
+// Proxy weight of key register i of half kb: the block's valid-row count
+// (0 = no key), stored as bytes; keys 4j .. 4j+3 share one 32-bit word.
+__device__ inline float proxy_weight(const uint8_t* wts, int kb, int i, int hh) {
+  const unsigned wd = *(const unsigned*)(wts + key_of(kb, i & ~3, hh));
+  return (float)((wd >> (8 * (i & 3))) & 0xFFu);
+}
+
 // Running-max update for one tile: the tile's largest logit (scaled, log2
 // units), and a rescale of O and the row sum when it exceeds the running max
 // by more than kRescaleSlack.
 template <int NKB, int MODE>
-__device__ inline void tile_max(const f32x16 (&s)[2], int nv, const float* offs, float c, int hh,
+__device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts, float c, int hh,
                                 State& st) {
   float t = -INFINITY;
   if (MODE == kModeProxy) {
+    // a proxy logit is offset by log2 of its weight (-inf for weight 0)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t = fmaxf(t, fmaf(s[kb][i], c, offs[key_of(kb, i, hh)]));
+      for (int i = 0; i < 16; ++i)
+        t = fmaxf(t, fmaf(s[kb][i], c, __log2f(proxy_weight(wts, kb, i, hh))));
     t = pair_max(t);
   } else if (MODE == kModePad) {
 #pragma unroll
@@ -289,10 +298,10 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const float* offs,
 // operand is the block's value total, so the numerator takes its probability
 // as is and only the denominator multiplies it by the block's valid-row count.
 template <int MODE, bool BF16>
-__device__ inline void half_probs(const f32x16& sk, int kb, int nv, const float* wts, float c,
+__device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_t* wts, float c,
                                   float nmc, int hh, float& lsum, unsigned (&pk)[8]) {
   if (MODE == kModeProxy) {
-    auto keyw = [&](int i) { return wts[key_of(kb, i, hh)]; };
+    auto keyw = [&](int i) { return proxy_weight(wts, kb, i, hh); };
     auto prob = [&](int i) {
       const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
       return keyw(i) > 0.0f ? e : 0.0f;
@@ -361,8 +370,7 @@ struct Ctx {
   const AttnParams* p;
   unsigned char* sk;
   unsigned char* sv;
-  const float* off;        // proxy logit offsets (log2 weight or -inf), per video block
-  const float* wt;         // proxy denominator weights (0 = no key), per video block
+  const uint8_t* wt;       // proxy denominator weights (valid rows, 0 = no key), per video block
   int b, h;
   int64_t bh_tiles;        // (b * heads + h) * nblk
   int64_t bh_proxy;        // (b * heads + h) * nproxy
@@ -416,14 +424,13 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
 
   const int nv = ent_nv(e);
   const bool px = kProxy && (MODE == kModeProxy || (MODE == kModeAny && (e & kEntProxy)));
-  const float* offs = kProxy ? x.off + kBlock * ent_id(e) : nullptr;
-  const float* wts = kProxy ? x.wt + kBlock * ent_id(e) : nullptr;
+  const uint8_t* wts = kProxy ? x.wt + kBlock * ent_id(e) : nullptr;
   if (kCompute) {
     if (MODE == kModeAny) {
-      if (px) tile_max<NKB, kModeProxy>(s, nv, offs, x.c, x.hh, st);
-      else tile_max<NKB, kModePad>(s, nv, offs, x.c, x.hh, st);
+      if (px) tile_max<NKB, kModeProxy>(s, nv, wts, x.c, x.hh, st);
+      else tile_max<NKB, kModePad>(s, nv, wts, x.c, x.hh, st);
     } else {
-      tile_max<NKB, MODE>(s, nv, offs, x.c, x.hh, st);
+      tile_max<NKB, MODE>(s, nv, wts, x.c, x.hh, st);
     }
   }
 
@@ -536,12 +543,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // (cell, block position in the sweep).
   const bool prefix_item = kProxy && qb < p.nprefix;
   const bool video_item = kProxy && !prefix_item;
-  int* tab = sDyn;                       // [table_cap] entries
-  int* ord = tab + p.table_cap;          // [table_cap] entries, processing order
-  int* key = ord + p.table_cap;          // [table_cap] sort keys
-  float* off = (float*)(key + p.table_cap);
-  float* wt = off + (kProxy ? p.nproxy * kBlock : 0);
-  unsigned* bits = (unsigned*)(wt + (kProxy ? p.nproxy * kBlock : 0));
+  // Dynamic LDS: the tile table (processing order, then sort keys) of `cap`
+  // entries; for proxy video items the per-block weights follow a table sized
+  // for video items, and a prefix item's longer table overlays them (prefix
+  // items take no weights).
+  const int vcap = kProxy ? p.nprefix + (p.sel_format == 0 ? p.idx_width : p.nvideo) + p.nproxy : 0;
+  const int cap = video_item ? vcap : p.table_cap;
+  int* ord = sDyn;                       // [cap] entries, processing order
+  int* key = ord + cap;                  // [cap] sort keys
+  uint8_t* wt = (uint8_t*)(sDyn + 2 * vcap);              // [nproxy * 64] weight (valid rows)
+  unsigned* bits = (unsigned*)(wt + p.nproxy * kBlock);   // [nproxy * 2] selected video blocks
   const int64_t bh_tiles = (int64_t)bh * p.nblk;
   // The index row: plain items and padded proxy rows read it in place; a BSR
   // row is a slice of the index list; a bitmask row is first expanded in LDS
@@ -550,6 +561,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int32_t* row = p.idx + (kProxy ? ((int64_t)bh * p.nvideo + (qb - p.nprefix)) * p.idx_width
                                        : (int64_t)item * p.idx_width);
   int width = p.idx_width;
+  // A bitmask row is read through the prefix counts of its words: wpos[wi]
+  // is the number of set bits before word wi (kept in the weight region
+  // until the weights are written), so its t-th selected block is found by a
+  // binary search and a bit select.  Bits past the last video block are
+  // ignored.
+  const bool bitmask_row = kProxy && video_item && p.sel_format == 1;
+  const uint32_t* mrow = nullptr;
+  int* wpos = (int*)wt;                  // [sel_words + 1]
+  auto word = [&](int wi) -> uint32_t {
+    const uint32_t m = mrow[wi];
+    const int valid = p.nvideo - 32 * wi;   // bits of this word that name a video block
+    return valid >= 32 ? m : (m & ((1u << valid) - 1u));
+  };
   if (kProxy && video_item && p.sel_format != 0) {
     const int64_t rid = (int64_t)bh * p.nvideo + (qb - p.nprefix);
     if (p.sel_format == 2) {
@@ -560,14 +584,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       width = min(end - beg, p.nvideo);
       row = p.sel_indices + beg;
     } else {
-      int* list = (int*)(bits + p.nproxy * 2);   // [nvideo] expanded row
-      int* wpos = list + p.nvideo;               // [sel_words + 1] first list position per word
-      const uint32_t* mrow = p.sel_mask + rid * p.sel_words;
-      auto word = [&](int wi) {
-        const uint32_t m = mrow[wi];
-        const int valid = p.nvideo - 32 * wi;   // bits of this word that name a video block
-        return valid >= 32 ? m : (m & ((1u << valid) - 1u));
-      };
+      mrow = p.sel_mask + rid * p.sel_words;
       if (tid == 0) {
         int acc = 0;
         for (int wi = 0; wi < p.sel_words; ++wi) {
@@ -577,19 +594,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         wpos[p.sel_words] = acc;
       }
       wg_barrier();
-      for (int wi = tid; wi < p.sel_words; wi += kThreads) {
-        uint32_t m = word(wi);
-        int pos = wpos[wi];
-        while (m) {
-          list[pos++] = 32 * wi + __builtin_ctz(m);
-          m &= m - 1u;
-        }
-      }
       width = __builtin_amdgcn_readfirstlane(wpos[p.sel_words]);
-      wg_barrier();
-      row = list;
     }
   }
+  auto sel_bit = [&](int tp) -> int {   // 0 <= tp < width
+    int lo = 0, hi = p.sel_words - 1;    // last word with wpos <= tp holds it
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wpos[mid] <= tp) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t m = word(lo);
+    for (int r = tp - wpos[lo]; r > 0; --r) m &= m - 1u;
+    return 32 * lo + __builtin_ctz(m);
+  };
   const int ncand = !kProxy ? p.idx_width : (prefix_item ? p.nblk : p.nprefix + width + p.nproxy);
   auto candidate = [&](int t) -> int {   // entry of candidate t, or -1
     int blk;
@@ -598,7 +616,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     } else if (prefix_item || t < p.nprefix) {
       blk = t;
     } else if (t < p.nprefix + width) {
-      const int s = row[t - p.nprefix];
+      const int s = bitmask_row ? sel_bit(t - p.nprefix) : row[t - p.nprefix];
       blk = (s >= 0 && s < p.nvideo) ? p.nprefix + s : -1;
     } else {
       const int pt = t - p.nprefix - width;
@@ -628,11 +646,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
   for (int t = tid; t < 2 * ncell + 1; t += kThreads) sCell[t] = 0;
-  for (int t = tid; t < ncand; t += kThreads) tab[t] = candidate(t);
   wg_barrier();
   const int start = sStart;
   for (int t = tid; t < ncand; t += kThreads) {
-    const int e = tab[t];
+    const int e = candidate(t);
     int k = 0x7FFFFFFF;
     if (e >= 0) {
       const int g = ent_group(e);
@@ -655,7 +672,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int ku = key[u];
       rank += (ku < kt) | ((ku == kt) & (u < t));
     }
-    ord[rank] = tab[t];
+    ord[rank] = candidate(t);   // entries are recomputed rather than kept in LDS
     atomicAdd(&ccnt[kt >> 20], 1);
   }
   wg_barrier();
@@ -672,24 +689,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // blocks) and their log2, which enters the running maximum so that the
     // weighted terms cannot overflow
     const int nbits = (p.nproxy * kBlock) / 32;
-    for (int t = tid; t < nbits; t += kThreads) bits[t] = 0u;
-    wg_barrier();
-    for (int t = tid; t < width; t += kThreads) {
-      const int s = row[t];
-      if (s >= 0 && s < p.nvideo) atomicOr(&bits[s >> 5], 1u << (s & 31));
+    if (bitmask_row) {
+      for (int t = tid; t < nbits; t += kThreads) bits[t] = t < p.sel_words ? word(t) : 0u;
+    } else {
+      for (int t = tid; t < nbits; t += kThreads) bits[t] = 0u;
+      wg_barrier();
+      for (int t = tid; t < width; t += kThreads) {
+        const int s = row[t];
+        if (s >= 0 && s < p.nvideo) atomicOr(&bits[s >> 5], 1u << (s & 31));
+      }
     }
     wg_barrier();
     for (int vblk = tid; vblk < p.nproxy * kBlock; vblk += kThreads) {
-      float o = -INFINITY, wv = 0.0f;
+      int wv = 0;
       if (vblk < p.nvideo) {
         const int nv = min(max(p.vbs[p.nprefix + vblk], 0), kBlock);
-        if (nv > 0 && !((bits[vblk >> 5] >> (vblk & 31)) & 1u)) {
-          o = __log2f((float)nv);
-          wv = (float)nv;
-        }
+        if (!((bits[vblk >> 5] >> (vblk & 31)) & 1u)) wv = nv;
       }
-      off[vblk] = o;
-      wt[vblk] = wv;
+      wt[vblk] = (uint8_t)wv;
     }
   }
   wg_barrier();
@@ -718,7 +735,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   x.p = &p;
   x.sk = sK;
   x.sv = sV;
-  x.off = off;
   x.wt = wt;
   x.b = b;
   x.h = h;
@@ -782,10 +798,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }  // namespace
 
 size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
-  size_t dyn = (size_t)p.table_cap * 4 * 3;
-  if (proxy) dyn += (size_t)p.nproxy * kBlock * 8 + (size_t)p.nproxy * 2 * 4;
-  if (proxy && p.sel_format == 1) dyn += (size_t)p.nvideo * 4 + (size_t)(p.sel_words + 1) * 4;
-  return dyn;
+  const size_t table = (size_t)p.table_cap * 8;
+  if (!proxy) return table;
+  const size_t vcap = (size_t)p.nprefix + (p.sel_format == 0 ? p.idx_width : p.nvideo) + p.nproxy;
+  const size_t video = vcap * 8 + (size_t)p.nproxy * kBlock + (size_t)p.nproxy * 2 * 4;
+  return table > video ? table : video;
 }
 
 namespace {

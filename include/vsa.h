@@ -34,7 +34,10 @@
  *     compile time, as in [RUN]).
  *   - Size limits (VSA_ERR_SHAPE otherwise): seq_len a positive multiple of 64
  *     with at most 2^20 - 1 cubes, 1 <= num_heads <= 65536, batch >= 1, and
- *     batch * num_heads * seq_len/64 < 2^31.
+ *     batch * num_heads * seq_len/64 < 2^31.  The per-workgroup tile table
+ *     takes 8 bytes per entry out of 32 KB of LDS: topk <= 4096 for vsa_fwd;
+ *     proxy calls need seq_len/64 <= 4096 and, for a video row, 8 bytes per
+ *     possible tile plus 72 bytes per 64 video blocks within the same 32 KB.
  */
 #ifndef VSA_H
 #define VSA_H
