@@ -233,6 +233,15 @@ __device__ inline void s_tile(const unsigned char* sk, const bf16x8 (&qop)[8], i
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], s[kb], 0, 0, 0);
     }
   }
+  // operand reads run half the chain ahead of the MFMAs
+  constexpr int kReads = 8 * NKB, kAhead = kReads / 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < kReads - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
 __device__ inline int key_of(int kb, int i, int hh) { return 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3); }
