@@ -3,6 +3,8 @@
 #include "vsa.h"
 #include "vsa_internal.h"
 
+#include <algorithm>
+
 #include <math.h>
 
 #include <atomic>
@@ -22,18 +24,30 @@ std::atomic<int> g_deterministic{0};
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t vt, pt, vf, pf, total;
+  size_t vt, pt, vf, pf, po, pl, total;
 };
 
+// Key blocks per prefix sub-item of the proxy forward: a prefix query block
+// attends to every block, so it is split into ranges of about the length of
+// a video block's tile list and the parts are merged afterwards.
+constexpr int32_t kPrefixSplit = 96;
+
+int prefix_splits(int64_t nblk) { return (int)((nblk + kPrefixSplit - 1) / kPrefixSplit); }
+
 // [V tiles B*H*nblk*16KB][proxy tiles B*H*nproxy*16KB][V flags][proxy flags]
-WsLayout ws_layout(int64_t batch, int64_t heads, int64_t nblk, int64_t nproxy) {
+// [prefix partial O/l: B*H*nprefix*psplit*64*128 fp32][their lse: ... *64 fp32]
+WsLayout ws_layout(int64_t batch, int64_t heads, int64_t nblk, int64_t nproxy,
+                   int64_t nprefix = 0, int64_t psplit = 0) {
   WsLayout l;
   const size_t bh = (size_t)batch * (size_t)heads;
+  const size_t subs = bh * (size_t)nprefix * (size_t)psplit;   // prefix sub-items
   l.vt = 0;
   l.pt = align_up(l.vt + bh * (size_t)nblk * kTileBytes, kWsAlign);
   l.vf = align_up(l.pt + bh * (size_t)nproxy * kTileBytes, kWsAlign);
   l.pf = align_up(l.vf + bh * (size_t)nblk, kWsAlign);
-  l.total = align_up(l.pf + bh * (size_t)nproxy, kWsAlign);
+  l.po = align_up(l.pf + bh * (size_t)nproxy, kWsAlign);
+  l.pl = align_up(l.po + subs * kBlock * kHeadDim * 4, kWsAlign);
+  l.total = align_up(l.pl + subs * kBlock * 4, kWsAlign);
   return l;
 }
 
@@ -56,6 +70,7 @@ AttnParams base_params(int32_t batch, int32_t seq_len, int32_t num_heads, float 
   p.seq = seq_len;
   p.heads = num_heads;
   p.nblk = seq_len / kBlock;
+  p.items_per_bh = p.nblk;
   p.n_items = batch * num_heads * p.nblk;
   p.items_per_xcd = (p.n_items + 7) / 8;
   p.c = sm_scale * 1.4426950408889634f;   // log2(e): softmax evaluated with exp2
@@ -98,7 +113,9 @@ extern "C" size_t vsa_fwd_proxy_workspace_size(int32_t batch, int32_t seq_len, i
   if (check_common(batch, seq_len, num_heads, head_dim) != VSA_OK) return 0;
   if (prefix_len <= 0 || prefix_len >= seq_len || prefix_len % kBlock != 0) return 0;
   const int64_t nvideo = (seq_len - prefix_len) / kBlock;
-  return ws_layout(batch, num_heads, seq_len / kBlock, (nvideo + kBlock - 1) / kBlock).total;
+  const int64_t nblk = seq_len / kBlock;
+  return ws_layout(batch, num_heads, nblk, (nvideo + kBlock - 1) / kBlock, prefix_len / kBlock,
+                   prefix_splits(nblk)).total;
 }
 
 namespace {
@@ -290,7 +307,11 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
   if (sel.format == 2 && sel.nnz < 0) return VSA_ERR_SHAPE;
   // rows of a bitmask or BSR selection may hold up to nvideo blocks
   const int row_cap = sel.format == 0 ? max_sel : nvideo;
-  const int table_cap = (nblk > nprefix + row_cap + nproxy) ? nblk : nprefix + row_cap + nproxy;
+  const int psplit = prefix_splits(nblk);
+  const int pwidth = std::min<int>(kPrefixSplit, nblk);
+  const int64_t items_per_bh = (int64_t)nprefix * psplit + nvideo;
+  if ((int64_t)batch * num_heads * items_per_bh > (int64_t)0x7FFFFFF0) return VSA_ERR_SHAPE;
+  const int table_cap = std::max(pwidth, nprefix + row_cap + nproxy);
   const int words = (nvideo + 31) / 32;
   // tile table of 8 bytes per entry; video items add a byte of weight per
   // video block and the selected-block bits
@@ -305,7 +326,7 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
       (sel.idx && !is_aligned(sel.idx, 4)) || (sel.mask && !is_aligned(sel.mask, 4)) ||
       (sel.indptr && !is_aligned(sel.indptr, 4)) || (sel.indices && !is_aligned(sel.indices, 4)))
     return VSA_ERR_ALIGN;
-  const WsLayout ws = ws_layout(batch, num_heads, nblk, nproxy);
+  const WsLayout ws = ws_layout(batch, num_heads, nblk, nproxy, nprefix, psplit);
   if (!workspace || workspace_bytes < ws.total) return VSA_ERR_WORKSPACE;
   if (!is_aligned(workspace, kWsAlign)) return VSA_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
@@ -355,7 +376,17 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
   p.nvideo = nvideo;
   p.nproxy = nproxy;
   p.table_cap = table_cap;
+  p.items_per_bh = (int)items_per_bh;
+  p.n_items = (int)((int64_t)batch * num_heads * items_per_bh);
+  p.items_per_xcd = (p.n_items + 7) / 8;
+  p.psplit = psplit;
+  p.pwidth = pwidth;
+  p.part_o = (float*)(wsb + ws.po);
+  p.part_lse = (float*)(wsb + ws.pl);
   if (launch_attn(p, true, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  if (launch_prefix_merge(p.part_o, p.part_lse, vbs, (uint16_t*)out, batch, seq_len, num_heads,
+                          nprefix, psplit, s) != hipSuccess)
+    return VSA_ERR_LAUNCH;
   return VSA_OK;
 }
 

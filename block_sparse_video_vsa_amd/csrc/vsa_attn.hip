@@ -57,6 +57,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
@@ -524,12 +525,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // XCD-aware item order: consecutive workgroup ids go round-robin to the 8
   // XCDs, so XCD x gets a contiguous run of items (whole heads) and its L2
-  // serves one head's K/V at a time.
+  // serves one head's K/V at a time.  A (batch, head) holds items_per_bh
+  // items: its query blocks, or in proxy mode psplit sub-items per prefix
+  // block (each over one range of pwidth key blocks) followed by the video
+  // blocks.
   const int xcd = (int)(blockIdx.x & 7);
   const int item = xcd * p.items_per_xcd + (int)(blockIdx.x >> 3);
   if (item >= p.n_items) return;
-  const int qb = item % p.nblk;
-  const int bh = item / p.nblk;
+  const int bh = item / p.items_per_bh;
+  const int ir = item - bh * p.items_per_bh;
+  int qb = ir, split = 0;
+  if (kProxy) {
+    const int nsub = p.nprefix * p.psplit;
+    if (ir < nsub) {
+      qb = ir / p.psplit;
+      split = ir - qb * p.psplit;
+    } else {
+      qb = p.nprefix + (ir - nsub);
+    }
+  }
   const int h = bh % p.heads;
   const int b = bh / p.heads;
   const int vq = min(max(p.vbs[qb], 0), kBlock);
@@ -617,12 +631,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int r = tp - wpos[lo]; r > 0; --r) m &= m - 1u;
     return 32 * lo + __builtin_ctz(m);
   };
-  const int ncand = !kProxy ? p.idx_width : (prefix_item ? p.nblk : p.nprefix + width + p.nproxy);
+  const int pfirst = split * p.pwidth;   // a prefix sub-item's first key block
+  const int ncand = !kProxy ? p.idx_width
+                            : (prefix_item ? min(p.pwidth, p.nblk - pfirst) : p.nprefix + width + p.nproxy);
   auto candidate = [&](int t) -> int {   // entry of candidate t, or -1
     int blk;
     if (!kProxy) {
       blk = row[t];
-    } else if (prefix_item || t < p.nprefix) {
+    } else if (prefix_item) {
+      blk = pfirst + t;
+    } else if (t < p.nprefix) {
       blk = t;
     } else if (t < p.nprefix + width) {
       const int s = bitmask_row ? sel_bit(t - p.nprefix) : row[t - p.nprefix];
@@ -783,6 +801,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // log sum exp(s * sm_scale) = (mc + log2 l) ln 2; -inf without keys.
     p.lse[(int64_t)bh * p.seq + (int64_t)qb * kBlock + qrow] =
         row_ok ? (st.mc + log2f(l_tot)) * 0.693147180559945f : -INFINITY;
+  }
+  if (prefix_item) {
+    // a prefix sub-item's share: O/l in fp32 and its row log-sum-exp, merged
+    // over the sub-items by prefix_merge_kernel
+    const int64_t prow = ((int64_t)(bh * p.nprefix + qb) * p.psplit + split) * kBlock + qrow;
+    if (hh == 0) p.part_lse[prow] = row_ok ? (st.mc + log2f(l_tot)) * 0.693147180559945f : -INFINITY;
+    float* orow32 = p.part_o + prow * kHeadDim + 4 * hh;
+    auto store_part = [&](const f32x16& acc, int db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 v4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[4 * a + r] * inv;
+          v4[r] = (row_ok && isfinite(v)) ? v : 0.0f;
+        }
+        *(f32x4*)(orow32 + 32 * db + 8 * a) = v4;
+      }
+    };
+    store_part(st.o0, 0);
+    store_part(st.o1, 1);
+    store_part(st.o2, 2);
+    store_part(st.o3, 3);
+    return;
   }
   uint16_t* orow = out_rows + (int64_t)qrow * row_stride + 4 * hh;
   auto store4 = [&](const f32x16& acc, int db) {

@@ -55,8 +55,13 @@ struct AttnParams {
   int nprefix;              // prefix blocks (proxy mode)
   int nvideo;               // video blocks (proxy mode)
   int nproxy;               // proxy tiles of 64 video blocks (proxy mode)
-  int n_items;              // batch * heads * nblk
+  int n_items;              // batch * heads * items_per_bh
   int items_per_xcd;
+  int items_per_bh;         // nblk, or (proxy) nprefix * psplit + nvideo
+  int psplit;               // proxy: sub-items per prefix query block
+  int pwidth;               // proxy: key blocks per prefix sub-item
+  float* part_o;            // proxy: prefix partial outputs O/l [B*H][nprefix][psplit][64][128]
+  float* part_lse;          // proxy: their row log-sum-exp [B*H][nprefix][psplit][64]
   int table_cap;            // tile-table capacity (entries)
   int sweep_slots;          // workgroups resident per XCD at once
   int nseg;                 // sweep segments per item (1..kMaxSeg)
@@ -75,6 +80,10 @@ int route_blocks_per_wg(int nblk);
 size_t route_lds_bytes(int nblk);
 hipError_t launch_route(const uint16_t* qmean, const uint16_t* kmean, const int32_t* vbs,
                         int32_t* out, int batch, int nblk, int heads, int topk, hipStream_t stream);
+// Merge of the prefix sub-items' partial results into the bf16 output rows.
+hipError_t launch_prefix_merge(const float* part_o, const float* part_lse, const int32_t* vbs,
+                               uint16_t* out, int batch, int seq, int heads, int nprefix,
+                               int psplit, hipStream_t stream);
 // Merge of two partial attention results over disjoint key sets.
 hipError_t launch_merge(const uint16_t* o1, const float* lse1, const uint16_t* o2, const float* lse2,
                         uint16_t* out, float* lse_out, int batch, int seq, int heads, int head_dim,

@@ -36,8 +36,10 @@
  *     with at most 2^20 - 1 cubes, 1 <= num_heads <= 65536, batch >= 1, and
  *     batch * num_heads * seq_len/64 < 2^31.  The per-workgroup tile table
  *     takes 8 bytes per entry out of 32 KB of LDS: topk <= 4096 for vsa_fwd;
- *     proxy calls need seq_len/64 <= 4096 and, for a video row, 8 bytes per
- *     possible tile plus 72 bytes per 64 video blocks within the same 32 KB.
+ *     proxy calls need, for a video row, 8 bytes per possible tile (prefix
+ *     blocks + row width + proxy tiles) plus 72 bytes per 64 video blocks
+ *     within the same 32 KB, and batch * num_heads * (prefix blocks *
+ *     ceil(seq_len/64 / 96) + video blocks) < 2^31.
  */
 #ifndef VSA_H
 #define VSA_H
@@ -152,7 +154,12 @@ vsa_status vsa_preprocess(const void* k, const void* v, const int32_t* vbs,
                           int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
                           vsa_stream_t stream);
 
-/* Workspace bytes vsa_fwd_proxy needs for this shape (0 if the shape is invalid). */
+/* Workspace bytes vsa_fwd_proxy needs for this shape (0 if the shape is invalid):
+ * the packed V and vsum tiles, and the partial results of the prefix query
+ * blocks.  A prefix block attends to every key block, so it runs as
+ * ceil(seq_len/64 / 96) parts over ranges of 96 key blocks; each part leaves
+ * O/l in fp32 and its row log-sum-exp (batch * num_heads * prefix blocks *
+ * parts * 64 * 129 floats), which a merge pass combines into the output. */
 size_t vsa_fwd_proxy_workspace_size(int32_t batch, int32_t seq_len, int32_t prefix_len,
                                     int32_t num_heads, int32_t head_dim);
 

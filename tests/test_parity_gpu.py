@@ -600,3 +600,37 @@ def test_route_topk_follows_sequential_rounding(dev):
     got = vsa.vsa_route_topk(to_dev(qm_b, dev, True), to_dev(km_b, dev, True), to_dev(vbs, dev), 2)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_proxy_prefix_split_and_merge(dev):
+    """200 blocks: each prefix query block runs as three sub-items over key
+    blocks [0, 96), [96, 192), [192, 200) and the parts are merged; the last
+    range holds only empty blocks (an empty part).  Full comparison with the
+    oracle, prefix rows included."""
+    rng = np.random.default_rng(27)
+    H, npb = 2, 3
+    nblk = 200
+    vbs = rng.integers(1, 65, nblk).astype(np.int32)
+    vbs[:npb] = [64, 40, 64]
+    vbs[192:] = 0
+    nv = nblk - npb
+    S = 64 * nblk
+    q, k, v = (_rand_bf16(rng, (1, S, H, D)) for _ in range(3))
+    width = 12
+    sel = np.full((1, H, nv, width), -1, np.int32)
+    for h in range(H):
+        for c in range(nv):
+            picks = rng.choice(nv, size=int(rng.integers(1, width + 1)), replace=False)
+            sel[0, h, c, :picks.size] = picks
+    dq, dk, dv, dvbs = (to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True),
+                        to_dev(vbs, dev))
+    km, vs = vsa.vsa_preprocess(dk, dv, dvbs)
+    km_o, vs_o = O.vsa_preprocess(k, v, vbs)
+    scale = np.float32(1 / math.sqrt(D))
+    out = from_dev(vsa.vsa_fwd_proxy(dq, dk, dv, to_dev(sel, dev), dvbs, km, vs, 64 * npb,
+                                     float(scale)))
+    o64 = O.vsa_fwd_proxy(q, k, v, sel, vbs, km_o, vs_o, 64 * npb, scale)
+    g = grade_full(out, o64, vbs)
+    print(f"proxy prefix split: {g}")
+    assert pad_rows_zero(out, vbs)
+    assert g.ok(), str(g)
