@@ -634,3 +634,20 @@ def test_proxy_prefix_split_and_merge(dev):
     print(f"proxy prefix split: {g}")
     assert pad_rows_zero(out, vbs)
     assert g.ok(), str(g)
+
+
+def test_side_stream_matches_default_stream(dev):
+    """The library enqueues on the caller's current stream: a call made under
+    a side stream (inputs written on that stream) equals the default-stream
+    result bit for bit (deterministic mode)."""
+    wl = W.generate("1")
+    ref = None
+    with vsa.deterministic():
+        ref = run_fwd(dev, wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+        side = torch.cuda.Stream(device=dev)
+        with torch.cuda.stream(side):
+            args = (to_dev(wl.q, dev, True), to_dev(wl.k, dev, True), to_dev(wl.v, dev, True),
+                    to_dev(wl.topk_idx, dev), to_dev(wl.vbs, dev))
+            out = vsa.vsa_fwd(*args, float(wl.sm_scale))
+        side.synchronize()
+    assert np.array_equal(from_dev(out), ref)
