@@ -532,8 +532,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int xcd = (int)(blockIdx.x & 7);
   const int item = xcd * p.items_per_xcd + (int)(blockIdx.x >> 3);
   if (item >= p.n_items) return;
-  const int bh = item / p.items_per_bh;
-  const int ir = item - bh * p.items_per_bh;
+  const int bh = kProxy ? item / p.items_per_bh : item / p.nblk;
+  const int ir = kProxy ? item - bh * p.items_per_bh : item % p.nblk;
   int qb = ir, split = 0;
   if (kProxy) {
     const int nsub = p.nprefix * p.psplit;

@@ -57,17 +57,18 @@ struct AttnParams {
   int nproxy;               // proxy tiles of 64 video blocks (proxy mode)
   int n_items;              // batch * heads * items_per_bh
   int items_per_xcd;
-  int items_per_bh;         // nblk, or (proxy) nprefix * psplit + nvideo
-  int psplit;               // proxy: sub-items per prefix query block
-  int pwidth;               // proxy: key blocks per prefix sub-item
-  float* part_o;            // proxy: prefix partial outputs O/l [B*H][nprefix][psplit][64][128]
-  float* part_lse;          // proxy: their row log-sum-exp [B*H][nprefix][psplit][64]
   int table_cap;            // tile-table capacity (entries)
   int sweep_slots;          // workgroups resident per XCD at once
   int nseg;                 // sweep segments per item (1..kMaxSeg)
   int seg_tiles;            // tiles of a typical item (sizes the segments)
   int deterministic;        // 1: sweep start from the workgroup index only
   float c;                  // sm_scale * log2(e)
+  // proxy prefix split (appended: the fields above keep their offsets)
+  int items_per_bh;         // nblk, or (proxy) nprefix * psplit + nvideo
+  int psplit;               // proxy: sub-items per prefix query block
+  int pwidth;               // proxy: key blocks per prefix sub-item
+  float* part_o;            // proxy: prefix partial outputs O/l [B*H][nprefix][psplit][64][128]
+  float* part_lse;          // proxy: their row log-sum-exp [B*H][nprefix][psplit][64]
 };
 
 hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream);
