@@ -16,7 +16,7 @@ namespace {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
 constexpr int64_t kMaxBlocks = (1 << 20) - 1;
-constexpr int32_t kMaxRouteBlocks = 7680;    // one sort row (8192 entries of 12 bytes) fits in LDS
+constexpr int32_t kMaxRouteBlocks = 7680;    // one score row (8 B per block) and the lists: 79 KB of LDS
 constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stays below 2^32 bytes
 
 std::atomic<int> g_deterministic{0};

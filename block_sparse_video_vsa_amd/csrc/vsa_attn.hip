@@ -578,9 +578,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   unsigned* bits = (unsigned*)(wt + p.nproxy * kBlock);   // [nproxy * 2] selected video blocks
   const int64_t bh_tiles = (int64_t)bh * p.nblk;
   // The index row: plain items and padded proxy rows read it in place; a BSR
-  // row is a slice of the index list; a bitmask row is first expanded in LDS
-  // into its set video blocks, ascending (bits past the last video block are
-  // ignored).
+  // row is a slice of the index list; a bitmask row is read through per-word
+  // counts of its set bits (below).
   const int32_t* row = p.idx + (kProxy ? ((int64_t)bh * p.nvideo + (qb - p.nprefix)) * p.idx_width
                                        : (int64_t)item * p.idx_width);
   int width = p.idx_width;

@@ -651,3 +651,20 @@ def test_side_stream_matches_default_stream(dev):
             out = vsa.vsa_fwd(*args, float(wl.sm_scale))
         side.synchronize()
     assert np.array_equal(from_dev(out), ref)
+
+
+def test_route_topk_at_the_block_limit(dev):
+    """7680 blocks (the largest routing shape: one score row per workgroup,
+    79 KB of LDS); sampled query rows against the oracle, which scores a row
+    from that row's mean and every key mean alone."""
+    rng = np.random.default_rng(28)
+    nblk, topk = 7680, 40
+    qm = W.f32_to_bf16_bits(rng.standard_normal((1, nblk, 1, 128)).astype(np.float32))
+    km = W.f32_to_bf16_bits(rng.standard_normal((1, nblk, 1, 128)).astype(np.float32))
+    vbs = rng.integers(0, 65, nblk).astype(np.int32)
+    got = vsa.vsa_route_topk(to_dev(qm, dev, True), to_dev(km, dev, True), to_dev(vbs, dev), topk)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    rows = np.array([0, 1, 2047, 4096, 7679])
+    want = O.route_topk(np.ascontiguousarray(qm[:, rows]), km, vbs, topk)
+    assert np.array_equal(got[:, :, rows], want)
