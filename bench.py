@@ -332,6 +332,7 @@ def bench_route(args, cfg, dev):
     qm = torch.empty((B, nb, H, D), dtype=torch.bfloat16, device=dev)
     km, scratch = torch.empty_like(qm), torch.empty_like(qm)
     idx = torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(vsa.route_workspace_size(B, nb, H), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -341,7 +342,7 @@ def bench_route(args, cfg, dev):
         vsa.vsa_preprocess(k, k, vbs, km, scratch)
         if ev is not None:
             ev[1].record(stream)
-        vsa.vsa_route_topk(qm, km, vbs, topk, out=idx)
+        vsa.vsa_route_topk(qm, km, vbs, topk, out=idx, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 

@@ -7,4 +7,5 @@ from .native import (VSAError, cube_vbs, deterministic, fwd_workspace_size,  # n
                      get_deterministic, load_library, proxy_workspace_size, set_deterministic,
                      vsa_fwd, vsa_fwd_lse, vsa_fwd_prepacked, vsa_fwd_proxy,
                      vsa_fwd_proxy_bitmask, vsa_fwd_proxy_bsr, vsa_merge,
-                     vsa_pack_values, vsa_preprocess, vsa_route_topk, vsa_tile, vsa_untile)
+                     vsa_pack_values, vsa_preprocess, route_workspace_size, vsa_route_topk,
+                     vsa_tile, vsa_untile)

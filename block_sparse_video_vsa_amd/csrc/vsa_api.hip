@@ -16,7 +16,7 @@ namespace {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
 constexpr int64_t kMaxBlocks = (1 << 20) - 1;
-constexpr int32_t kMaxRouteBlocks = 7680;    // one score row (8 B per block) and the lists: 79 KB of LDS
+constexpr int32_t kMaxRouteBlocks = 7680;    // one (batch, head) of scores: 472 MB of workspace
 constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stays below 2^32 bytes
 
 std::atomic<int> g_deterministic{0};
@@ -505,21 +505,30 @@ extern "C" vsa_status vsa_untile(const void* x_tiled, void* x, int32_t batch, in
              : VSA_ERR_LAUNCH;
 }
 
+extern "C" size_t vsa_route_workspace_size(int32_t batch, int32_t num_blocks, int32_t num_heads) {
+  if (batch < 1 || num_heads < 1 || num_blocks < 1 || num_blocks > kMaxRouteBlocks) return 0;
+  if ((int64_t)batch * num_heads * num_blocks >= ((int64_t)1 << 31)) return 0;
+  return align_up(route_workspace_bytes(batch, num_heads, num_blocks), kWsAlign);
+}
+
 extern "C" vsa_status vsa_route_topk(const void* qmean, const void* kmean, const int32_t* vbs,
                                      int32_t* topk_idx, int32_t batch, int32_t num_blocks,
                                      int32_t num_heads, int32_t head_dim, int32_t topk,
-                                     vsa_stream_t stream) {
+                                     void* workspace, size_t workspace_bytes, vsa_stream_t stream) {
   if (!qmean || !kmean || !vbs || !topk_idx) return VSA_ERR_NULL;
   if (head_dim != kHeadDim) return VSA_ERR_UNSUPPORTED;
   if (batch < 1 || num_heads < 1 || num_blocks < 1 || num_blocks > kMaxRouteBlocks ||
       topk < 1 || topk > num_blocks)
     return VSA_ERR_SHAPE;
   if ((int64_t)batch * num_heads * num_blocks * topk >= ((int64_t)1 << 31)) return VSA_ERR_SHAPE;
-  if (!is_aligned(qmean, 2) || !is_aligned(kmean, 16) || !is_aligned(vbs, 4) ||
+  if (!is_aligned(qmean, 16) || !is_aligned(kmean, 16) || !is_aligned(vbs, 4) ||
       !is_aligned(topk_idx, 4))
     return VSA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < vsa_route_workspace_size(batch, num_blocks, num_heads))
+    return VSA_ERR_WORKSPACE;
+  if (!is_aligned(workspace, kWsAlign)) return VSA_ERR_ALIGN;
   return launch_route((const uint16_t*)qmean, (const uint16_t*)kmean, vbs, topk_idx, batch,
-                      num_blocks, num_heads, topk, (hipStream_t)stream) == hipSuccess
+                      num_blocks, num_heads, topk, (double*)workspace, (hipStream_t)stream) == hipSuccess
              ? VSA_OK
              : VSA_ERR_LAUNCH;
 }

@@ -77,10 +77,13 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
 // Routing: top-k key blocks by block-mean scores.
-int route_blocks_per_wg(int nblk);
-size_t route_lds_bytes(int nblk);
+// Routing: top-k key blocks by block-mean scores, through an fp64 score
+// workspace that holds route_pairs_per_chunk (batch, head) pairs at a time.
+int route_pairs_per_chunk(int batch, int heads, int nblk);
+size_t route_workspace_bytes(int batch, int heads, int nblk);
 hipError_t launch_route(const uint16_t* qmean, const uint16_t* kmean, const int32_t* vbs,
-                        int32_t* out, int batch, int nblk, int heads, int topk, hipStream_t stream);
+                        int32_t* out, int batch, int nblk, int heads, int topk, double* scores,
+                        hipStream_t stream);
 // Merge of the prefix sub-items' partial results into the bf16 output rows.
 hipError_t launch_prefix_merge(const float* part_o, const float* part_lse, const int32_t* vbs,
                                uint16_t* out, int batch, int seq, int heads, int nprefix,

@@ -14,25 +14,32 @@
 // products in that order: scores (and therefore the chosen indices) are
 // reproducible to the last bit.
 //
-// One workgroup of 256 threads handles QB query blocks of one (batch, head).
-// Scores: thread t streams KPT mean key rows (t, t + 256, ...) through
-// registers and runs QB x KPT independent multiply-add chains; the QB mean
-// query values of one d are read from LDS once (the same address in every
-// lane) and feed KPT chains each, which keeps the LDS return path below the
-// float64 FMA rate.  Selection, one wavefront per query block, no workgroup
-// barriers:
-//   1. radix select over order-preserving 64-bit codes of the scores, 8 bits
-//      at a time from the top, until the bin holding the k-th largest score
-//      has at most a few more entries than still needed; the bin's lower edge
-//      is a bound T at or below the k-th largest score;
-//   2. every block with a score at or above T is a candidate.  A block that
-//      outranks a candidate is a candidate too, so a candidate's exact rank in
-//      (score descending, index ascending) order is counted over the
-//      candidates alone, kept in LDS in index order; it is written out when
-//      the rank is below topk.  Every block of rank below topk is a
-//      candidate, so each output slot is written once.  When the candidates
-//      do not fit the list (massive ties, very large topk) ranks are counted
-//      over the whole row instead.
+// Two kernels per chunk of (batch, head) pairs, through a workspace of fp64
+// scores:
+//   route_score_kernel: one workgroup per 128 x 128 tile of (query block, key
+//     block) scores.  The bf16 means are staged 32 values of d at a time in
+//     LDS as fp32 (exact), d-major; each of the 16 x 16 threads keeps an 8 x 8
+//     tile of fp64 sums in registers and adds d = 0..127 in order, so every
+//     score is the same sequence of roundings as one running sum.  Empty key
+//     blocks (vbs = 0) are stored as -inf.
+//   route_select_kernel: one wavefront per query block, over its score row:
+//     0. a bound from a sample: each lane takes one block of the row, the 64
+//        sampled scores are sorted across lanes, and the value a few places
+//        past the expected position of the k-th largest is a bound T.  When
+//        between k and 256 blocks reach it, step 2 runs on them directly;
+//        otherwise:
+//     1. radix select over order-preserving 64-bit codes of the scores, 8 bits
+//        at a time from the top, until the bin holding the k-th largest score
+//        has at most a few more entries than still needed; the bin's lower
+//        edge is a bound T at or below the k-th largest score;
+//     2. every block with a score at or above T is a candidate.  A block that
+//        outranks a candidate is a candidate too, so a candidate's exact rank
+//        in (score descending, index ascending) order is its position among
+//        the candidates alone: up to 256 of them are listed in LDS and sorted
+//        by a bitonic network in registers, and the first topk are written.
+//        Every block of rank below topk is a candidate, so each output slot
+//        is written once.  When the candidates do not fit the list (massive
+//        ties, very large topk) ranks are counted over the whole row instead.
 #include "vsa_internal.h"
 
 #include <math.h>
@@ -45,48 +52,13 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kHistBins = 256;
 constexpr int kCandList = 256;         // per-wavefront candidate list (scores and block ids)
 constexpr int kExtraCandidates = 32;   // stop refining the bound once this close
-constexpr int kBufferWord3 = 0x00020000;   // buffer resource flags for raw (untyped) loads
+constexpr int kSampleSlack = 4;        // sample places added below the expected k-th
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) double f64x2;
 
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
-
-// Buffer loads are calls the compiler keeps where they stand (a plain load's
-// prefetch into a register ring gets folded back into a load at the point of
-// use), and the hardware returns zeros past num_records.
-__device__ inline u32x4 load_piece(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, int piece) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(voff + 16u * piece), 0, 0);
-}
-
-// Adds 4 products (d = d0 .. d0 + 3, values w[half*2], w[half*2 + 1] of each
-// key's piece) to each of the QB x KPT chains.
-template <int QB, int KPT>
-__device__ __attribute__((always_inline)) inline void score_quarter(double (&acc)[QB][KPT],
-                                                                    const u32x4 (&w)[KPT], int half,
-                                                                    const double* qi) {
-  double qv[4 * QB];
-#pragma unroll
-  for (int t = 0; t < 4 * QB; ++t) qv[t] = qi[t];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const unsigned word = w[c][2 * half + e / 2];
-      const double kv = (double)bf16f((uint16_t)(word >> (16 * (e % 2))));
-#pragma unroll
-      for (int r = 0; r < QB; ++r) acc[r][c] = fma(qv[e * QB + r], kv, acc[r][c]);
-    }
-  }
-}
-
-template <int QB, int KPT>
-__device__ __attribute__((always_inline)) inline void score_piece(double (&acc)[QB][KPT],
-                                                                  const u32x4 (&w)[KPT],
-                                                                  const double* qi) {
-  score_quarter<QB, KPT>(acc, w, 0, qi);
-  __builtin_amdgcn_sched_barrier(0);   // half a piece's query values live at a time
-  score_quarter<QB, KPT>(acc, w, 1, qi + 4 * QB);
-}
 
 // Orders doubles as unsigned integers (no NaN here; zeros are +0).
 __device__ inline uint64_t order_code(double s) {
@@ -114,6 +86,12 @@ __device__ inline int wave_inclusive_sum(int v, int lane) {
   return v;
 }
 
+// (score, block id) order of the output: a higher score first, equal scores
+// by the lower block id.
+__device__ inline bool before(double sa, int ia, double sb, int ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
+
 // Number of entries of list[0, n) that come before (se, position pe): a higher
 // score, or an equal score at a lower position (positions follow block ids).
 __device__ __attribute__((always_inline)) inline int rank_in(const double* __restrict__ list, int n,
@@ -127,18 +105,153 @@ __device__ __attribute__((always_inline)) inline int rank_in(const double* __res
   return rank;
 }
 
-// Top-k of one row of scores by one wavefront.
+// Sorts the listed candidates of one row into (score descending, index
+// ascending) order with a bitonic network over 64 * E positions, E per lane
+// (position E * lane + s in register s; positions past the list are padding
+// that sorts last), and writes the first topk block ids.  A candidate's sorted
+// position is its rank in the whole row, since every block that outranks a
+// candidate is a candidate.
+template <int E>
+__device__ __attribute__((always_inline)) inline void sort_candidates(
+    const double* __restrict__ cs, const int* __restrict__ ci, int listed, int topk,
+    int32_t* __restrict__ orow, int lane) {
+  double sv[E];
+  int iv[E];
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    const int p = E * lane + s;
+    sv[s] = p < listed ? cs[p] : -INFINITY;
+    iv[s] = p < listed ? ci[p] : 0x7FFFFFFF - p;   // distinct, after every block id
+  }
+  constexpr int N = 64 * E;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {   // both positions in this lane's registers
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+          if (s & j) continue;
+          const int t = s | j;
+          const bool asc = ((E * lane + s) & k) == 0;   // the lower position takes the first
+          const bool swap = asc ? before(sv[t], iv[t], sv[s], iv[s]) : before(sv[s], iv[s], sv[t], iv[t]);
+          if (swap) {
+            const double ts = sv[s];
+            const int ti = iv[s];
+            sv[s] = sv[t];
+            iv[s] = iv[t];
+            sv[t] = ts;
+            iv[t] = ti;
+          }
+        }
+      } else {       // partner position in lane ^ (j / E), same register
+        const int lm = j / E;
+        const bool lower = (lane & lm) == 0;
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+          const double os = __shfl_xor(sv[s], lm, 64);
+          const int oi = __shfl_xor(iv[s], lm, 64);
+          const bool asc = ((E * lane + s) & k) == 0;
+          const bool keep_first = lower == asc;
+          const bool mine_first = before(sv[s], iv[s], os, oi);
+          if (keep_first != mine_first) {
+            sv[s] = os;
+            iv[s] = oi;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    const int p = E * lane + s;
+    if (p < listed && p < topk) orow[p] = iv[s];
+  }
+}
+
+// The 64 lanes' values in descending order (bitonic network across lanes):
+// lane p ends with the p-th largest.
+__device__ __attribute__((always_inline)) inline uint64_t wave_sort_desc(uint64_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned lo = __shfl_xor((unsigned)v, j, 64);
+      const unsigned hi = __shfl_xor((unsigned)(v >> 32), j, 64);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;     // this block of the network puts the largest first
+      const bool keep_larger = lower == desc;
+      v = keep_larger ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
+// Top-k of one row of scores (in memory) by one wavefront.
 __device__ __attribute__((always_inline)) inline void select_row(
     const double* __restrict__ row, int n, int topk, int* __restrict__ hist,
     double* __restrict__ cs, int* __restrict__ ci, int32_t* __restrict__ orow, int lane) {
+  const int nchunks = (n + 63) >> 6;
+  // value of this lane's block in chunk c (-inf past the row)
+  auto val = [&](int c) -> double {
+    const int e = c * 64 + lane;
+    return e < n ? row[e] : -INFINITY;
+  };
+  auto chunks = [&](auto f) {
+    for (int c = 0; c < nchunks; ++c) f(c);
+  };
+  // candidates (finite, code >= t) listed in index order; returns their count
+  auto list_from = [&](uint64_t t) {
+    int listed = 0;
+    chunks([&](int c) {
+      const double v = val(c);
+      const bool is_cand = v != -INFINITY && order_code(v) >= t;
+      const uint64_t m = __ballot(is_cand);
+      const int at = listed + lanes_below(m);
+      if (is_cand && at < kCandList) {
+        cs[at] = v;
+        ci[at] = c * 64 + lane;
+      }
+      listed += __popcll(m);
+    });
+    wave_sync();
+    return listed;
+  };
+  auto sort_listed = [&](int listed) {
+    if (listed <= 64) sort_candidates<1>(cs, ci, listed, topk, orow, lane);
+    else if (listed <= 128) sort_candidates<2>(cs, ci, listed, topk, orow, lane);
+    else sort_candidates<4>(cs, ci, listed, topk, orow, lane);
+    wave_sync();   // the lists are refilled by this wavefront's next row
+  };
+
   // eligible blocks (finite score) rank before every empty one
   int local = 0;
-  for (int e = lane; e < n; e += 64) local += row[e] != -INFINITY;
+  chunks([&](int c) { local += val(c) != -INFINITY; });
   int eligible = wave_inclusive_sum(local, lane);
   eligible = __shfl(eligible, 63, 64);
   for (int t = eligible + lane; t < topk; t += 64) orow[t] = -1;
   int need = min(topk, eligible);
   if (need == 0) return;
+
+  // 0. fast path: a threshold from a sample.  Lane l samples block l*n/64;
+  // the sorted sample's value a few places past the expected position of the
+  // need-th largest is a bound T; if between need and kCandList blocks reach
+  // it, they hold every block of rank below need and are sorted directly.
+  {
+    const double s = row[(int)(((int64_t)lane * n) >> 6)];
+    const uint64_t sc = wave_sort_desc(s != -INFINITY ? order_code(s) : 0ull, lane);
+    const int q = min(63, (int)(((int64_t)need * 64 + eligible - 1) / eligible) + kSampleSlack);
+    const unsigned tlo = __shfl((unsigned)sc, q, 64), thi = __shfl((unsigned)(sc >> 32), q, 64);
+    const uint64_t t = ((uint64_t)thi << 32) | tlo;
+    if (t != 0ull) {
+      const int listed = list_from(t);
+      if (listed >= need && listed <= kCandList) {
+        sort_listed(listed);
+        return;
+      }
+    }
+  }
 
   // 1. lower bound on the need-th largest code
   uint64_t prefix = 0, pmask = 0;
@@ -146,11 +259,11 @@ __device__ __attribute__((always_inline)) inline void select_row(
 #pragma unroll
     for (int i = 0; i < kHistBins / 64; ++i) hist[lane * (kHistBins / 64) + i] = 0;
     wave_sync();
-    for (int e = lane; e < n; e += 64) {
-      const double s = row[e];
-      const uint64_t c = order_code(s);
-      if (s != -INFINITY && (c & pmask) == prefix) atomicAdd(&hist[(int)((c >> shift) & 0xFF)], 1);
-    }
+    chunks([&](int c) {
+      const double s = val(c);
+      const uint64_t code = order_code(s);
+      if (s != -INFINITY && (code & pmask) == prefix) atomicAdd(&hist[(int)((code >> shift) & 0xFF)], 1);
+    });
     wave_sync();
     // lane L owns bins 255 - 4L .. 252 - 4L, highest first
     int cnt[kHistBins / 64];
@@ -187,186 +300,172 @@ __device__ __attribute__((always_inline)) inline void select_row(
     if (in_bin - need <= kExtraCandidates) break;
   }
 
-  // 2. candidates (code >= prefix) listed in index order
-  int listed = 0;
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const int e = e0 + lane;
-    double s = -INFINITY;
-    bool is_cand = false;
-    if (e < n) {
-      s = row[e];
-      is_cand = s != -INFINITY && order_code(s) >= prefix;
-    }
-    const uint64_t m = __ballot(is_cand);
-    const int at = listed + lanes_below(m);
-    if (is_cand && at < kCandList) {
-      cs[at] = s;
-      ci[at] = e;
-    }
-    listed += __popcll(m);
-  }
-  wave_sync();
+  // 2. candidates (code >= prefix) listed in index order and sorted; past
+  // kCandList of them, ranks are counted over the whole row
+  const int listed = list_from(prefix);
   if (listed <= kCandList) {
-    for (int c = lane; c < listed; c += 64) {
-      const int rank = rank_in(cs, listed, cs[c], c);
-      if (rank < topk) orow[rank] = ci[c];
-    }
-  } else {
-    for (int e0 = 0; e0 < n; e0 += 64) {
-      const int e = e0 + lane;
-      if (e < n) {
-        const double s = row[e];
-        if (s != -INFINITY && order_code(s) >= prefix) {
-          const int rank = rank_in(row, n, s, e);
-          if (rank < topk) orow[rank] = e;
-        }
-      }
-    }
+    sort_listed(listed);
+    return;
   }
-  wave_sync();   // the lists are refilled by this wavefront's next row
+  chunks([&](int c) {
+    const double s = val(c);
+    if (s != -INFINITY && order_code(s) >= prefix) {
+      const int e = c * 64 + lane;
+      const int rank = rank_in(row, n, s, e);
+      if (rank < topk) orow[rank] = e;
+    }
+  });
+  wave_sync();
 }
 
-// LDS allows two workgroups per CU at most (two waves per SIMD), so the
-// compiler may spend registers on loads in flight instead of occupancy.
-template <int QB, int KPT>
-__global__ __launch_bounds__(kRouteThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void route_kernel(
-    const uint16_t* __restrict__ qmean, const uint16_t* kmean, const int32_t* __restrict__ vbs,
-    int32_t* __restrict__ out, int nblk, int heads, int topk) {
-  extern __shared__ double sRoute[];
-  double* score = sRoute;                                     // [QB][nblk]
-  double* qd = score + (size_t)QB * nblk;                     // [128][QB] mean query, d-major
-  double* cs = qd + kHeadDim * QB;                            // [waves][kCandList]
-  int* ci = (int*)(cs + kRouteWaves * kCandList);             // [waves][kCandList]
-  int* hist = ci + kRouteWaves * kCandList;                   // [waves][256]
-  const int groups = (nblk + QB - 1) / QB;
-  const int g = blockIdx.x % groups;
-  const int bh = blockIdx.x / groups;
-  const int h = bh % heads;
-  const int b = bh / heads;
-  const int q0 = g * QB;
-  const int nq = min(QB, nblk - q0);
+constexpr int kScoreTile = 128;   // query and key blocks per score tile
+constexpr int kDChunk = 32;       // values of d staged per step
+
+__global__ __launch_bounds__(kRouteThreads) void route_score_kernel(const uint16_t* __restrict__ qmean,
+                                                                    const uint16_t* __restrict__ kmean,
+                                                                    const int32_t* __restrict__ vbs,
+                                                                    double* __restrict__ scores, int bh0,
+                                                                    int nblk, int heads, int tiles) {
+  __shared__ __attribute__((aligned(16))) float sQ[kDChunk][kScoreTile];
+  __shared__ __attribute__((aligned(16))) float sK[kDChunk][kScoreTile];
+  const int per_pair = tiles * tiles;
+  const int g = blockIdx.x / per_pair;
+  const int t = blockIdx.x - g * per_pair;
+  const int i0 = (t / tiles) * kScoreTile, j0 = (t % tiles) * kScoreTile;
+  const int bh = bh0 + g;
+  const int h = bh % heads, b = bh / heads;
   const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;   // rows i0 + 8ty .., columns j0 + 8tx ..
 
-  for (int i = tid; i < QB * kHeadDim; i += kRouteThreads) {
-    const int r = i / kHeadDim, d = i % kHeadDim;
-    qd[d * QB + r] =
-        r < nq ? (double)bf16f(qmean[(((int64_t)b * nblk + q0 + r) * heads + h) * kHeadDim + d]) : 0.0;
-  }
-  __syncthreads();
+  double acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0;
 
-  // ---- scores -----------------------------------------------------------
-  const int64_t row_stride = (int64_t)heads * kHeadDim * 2;              // bytes between key rows
-  const unsigned voff = (unsigned)((int64_t)tid * row_stride);           // < 2^32 for heads <= 65536
-  for (int j0 = 0; j0 < nblk; j0 += kRouteThreads * KPT) {
-    __amdgpu_buffer_rsrc_t rsrc[KPT];
+  // 128 rows x 32 values = 512 pieces of 16 bytes per operand and chunk; four
+  // consecutive threads read one row's 64 contiguous bytes.  The next chunk's
+  // pieces are loaded into registers while the current one is used.
+  constexpr int kPieces = kScoreTile * (kDChunk / 8) / kRouteThreads;   // 2 per thread
+  u32x4 nq[kPieces], nk[kPieces];
+  auto fetch = [&](int d0) {
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const int first = min(j0 + c * kRouteThreads, nblk);               // rows first .. first+rows-1
-      const int rows = min(kRouteThreads, nblk - first);
-      const int64_t span = rows > 0 ? (int64_t)(rows - 1) * row_stride + kHeadDim * 2 : 0;
-      rsrc[c] = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kmean + (((int64_t)b * nblk + first) * heads + h) * kHeadDim), (short)0,
-          (int)(unsigned)min(span, (int64_t)0xFFFFFFFF), kBufferWord3);
+    for (int s = 0; s < kPieces; ++s) {
+      const int pc = tid + s * kRouteThreads;
+      const int r = pc >> 2, part = pc & 3;
+      nq[s] = (u32x4){0u, 0u, 0u, 0u};
+      nk[s] = (u32x4){0u, 0u, 0u, 0u};
+      if (i0 + r < nblk)
+        nq[s] = *(const u32x4*)(qmean + (((int64_t)b * nblk + i0 + r) * heads + h) * kHeadDim + d0 + 8 * part);
+      if (j0 + r < nblk)
+        nk[s] = *(const u32x4*)(kmean + (((int64_t)b * nblk + j0 + r) * heads + h) * kHeadDim + d0 + 8 * part);
     }
-    double acc[QB][KPT];
+  };
+  fetch(0);
+  for (int d0 = 0; d0 < kHeadDim; d0 += kDChunk) {
+    __syncthreads();   // the previous chunk is consumed
 #pragma unroll
-    for (int r = 0; r < QB; ++r)
+    for (int s = 0; s < kPieces; ++s) {
+      const int pc = tid + s * kRouteThreads;
+      const int r = pc >> 2, part = pc & 3;
 #pragma unroll
-      for (int c = 0; c < KPT; ++c) acc[r][c] = 0.0;
-    // 16-byte pieces of 8 values in a ring of two per key: each slot is used,
-    // then refilled with the piece two ahead (rows past the end read zeros)
-    u32x4 pa[KPT], pb[KPT];
-#pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      pa[c] = load_piece(rsrc[c], voff, 0);
-      pb[c] = load_piece(rsrc[c], voff, 1);
-    }
-#pragma unroll 1
-    for (int i = 0; i < kHeadDim / 8; i += 2) {
-      const int last = kHeadDim / 8 - 1;   // the final round refills in-row, unused
-      score_piece<QB, KPT>(acc, pa, qd + 8 * i * QB);
-#pragma unroll
-      for (int c = 0; c < KPT; ++c) pa[c] = load_piece(rsrc[c], voff, min(i + 2, last));
-      __builtin_amdgcn_sched_barrier(0);
-      score_piece<QB, KPT>(acc, pb, qd + 8 * (i + 1) * QB);
-#pragma unroll
-      for (int c = 0; c < KPT; ++c) pb[c] = load_piece(rsrc[c], voff, min(i + 3, last));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const int j = j0 + c * kRouteThreads + tid;
-      if (j < nblk) {
-        const bool live = vbs[j] > 0;
-#pragma unroll
-        for (int r = 0; r < QB; ++r)
-          if (r < nq) score[(size_t)r * nblk + j] = live ? acc[r][c] + 0.0 : -INFINITY;
+      for (int e = 0; e < 8; ++e) {
+        sQ[8 * part + e][r] = bf16f((uint16_t)(nq[s][e / 2] >> (16 * (e % 2))));
+        sK[8 * part + e][r] = bf16f((uint16_t)(nk[s][e / 2] >> (16 * (e % 2))));
       }
     }
+    __syncthreads();
+    if (d0 + kDChunk < kHeadDim) fetch(d0 + kDChunk);
+#pragma unroll 2
+    for (int d = 0; d < kDChunk; ++d) {
+      const f32x4 q0 = *(const f32x4*)&sQ[d][8 * ty], q1 = *(const f32x4*)&sQ[d][8 * ty + 4];
+      const f32x4 k0 = *(const f32x4*)&sK[d][8 * tx], k1 = *(const f32x4*)&sK[d][8 * tx + 4];
+      double qd[8], kd[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qd[e] = (double)q0[e];
+        qd[4 + e] = (double)q1[e];
+        kd[e] = (double)k0[e];
+        kd[4 + e] = (double)k1[e];
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[a][c] = fma(qd[a], kd[c], acc[a][c]);
+    }
   }
-  __syncthreads();
 
-  // ---- selection: one wavefront per query block ---------------------------
-  const int wave = tid / 64, lane = tid % 64;
-  for (int r = wave; r < nq; r += kRouteWaves)
-    select_row(score + (size_t)r * nblk, nblk, topk, hist + wave * kHistBins,
-               cs + wave * kCandList, ci + wave * kCandList,
-               out + ((int64_t)bh * nblk + q0 + r) * topk, lane);
+  double* srow = scores + (size_t)g * nblk * nblk;
+  const int jb = j0 + 8 * tx;
+  bool live[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) live[c] = jb + c < nblk && vbs[jb + c] > 0;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + 8 * ty + a;
+    if (i >= nblk) continue;
+    double* dst = srow + (size_t)i * nblk + jb;
+    // paired 16-byte stores where the absolute element index is even
+    if (jb + 8 <= nblk && ((((size_t)g * nblk + i) * nblk + jb) & 1) == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; c += 2)
+        *(f64x2*)(dst + c) = (f64x2){live[c] ? acc[a][c] + 0.0 : -INFINITY,
+                                     live[c + 1] ? acc[a][c + 1] + 0.0 : -INFINITY};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (jb + c < nblk) dst[c] = live[c] ? acc[a][c] + 0.0 : -INFINITY;
+    }
+  }
 }
 
-int pick_qb(int nblk) {
-  // score rows of 8 bytes per block, at most 48 KB of them, at most 8 rows
-  const int fit = (int)(49152 / ((size_t)nblk * 8));
-  return fit >= 8 ? 8 : fit >= 4 ? 4 : fit >= 2 ? 2 : 1;
-}
-
-// key rows per thread: enough to cover the row in one pass, at most 4
-int pick_kpt(int nblk) {
-  const int k = (nblk + kRouteThreads - 1) / kRouteThreads;
-  return k > 4 ? 4 : k;
+__global__ __launch_bounds__(kRouteThreads) void route_select_kernel(const double* __restrict__ scores,
+                                                                     int32_t* __restrict__ out, int bh0,
+                                                                     int rows, int nblk, int topk) {
+  __shared__ int hist[kRouteWaves][kHistBins];
+  __shared__ double cs[kRouteWaves][kCandList];
+  __shared__ int ci[kRouteWaves][kCandList];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int r = blockIdx.x * kRouteWaves + wave;   // row of the chunk: g * nblk + i
+  if (r >= rows) return;                          // per wavefront: no workgroup barriers below
+  const double* row = scores + (size_t)r * nblk;
+  int32_t* orow = out + ((int64_t)bh0 * nblk + r) * topk;
+  select_row(row, nblk, topk, hist[wave], cs[wave], ci[wave], orow, lane);
 }
 
 }  // namespace
 
-int route_blocks_per_wg(int nblk) { return pick_qb(nblk); }
-
-size_t route_lds_bytes(int nblk) {
-  const int qb = pick_qb(nblk);
-  return (size_t)qb * nblk * 8 + (size_t)kHeadDim * qb * 8 +
-         (size_t)kRouteWaves * (kCandList * 12 + kHistBins * 4);
+int route_pairs_per_chunk(int batch, int heads, int nblk) {
+  const size_t per_pair = (size_t)nblk * nblk * 8;
+  const size_t cap = (size_t)256 << 20;   // score workspace target: 256 MB
+  size_t g = cap / per_pair;
+  if (g < 1) g = 1;
+  const size_t pairs = (size_t)batch * heads;
+  return (int)(g < pairs ? g : pairs);
 }
 
-template <int QB, int KPT>
-static void launch_one(dim3 grid, size_t lds, hipStream_t stream, const uint16_t* qmean,
-                       const uint16_t* kmean, const int32_t* vbs, int32_t* out, int nblk, int heads,
-                       int topk) {
-  hipLaunchKernelGGL((route_kernel<QB, KPT>), grid, dim3(kRouteThreads), lds, stream, qmean, kmean,
-                     vbs, out, nblk, heads, topk);
+size_t route_workspace_bytes(int batch, int heads, int nblk) {
+  return (size_t)route_pairs_per_chunk(batch, heads, nblk) * nblk * nblk * 8;
 }
 
 hipError_t launch_route(const uint16_t* qmean, const uint16_t* kmean, const int32_t* vbs,
-                        int32_t* out, int batch, int nblk, int heads, int topk,
+                        int32_t* out, int batch, int nblk, int heads, int topk, double* scores,
                         hipStream_t stream) {
-  const int qb = pick_qb(nblk);
-  const int kpt = pick_kpt(nblk);
-  const int groups = (nblk + qb - 1) / qb;
-  const int64_t blocks = (int64_t)batch * heads * groups;
-  if (blocks == 0) return hipSuccess;
-  const size_t lds = route_lds_bytes(nblk);
-  const dim3 grid((unsigned)blocks);
-  // qb = 8 only for nblk <= 768 (kpt <= 3); smaller qb means nblk > 768 (kpt = 4)
-  if (qb == 8) {
-    if (kpt == 1) launch_one<8, 1>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
-    else if (kpt == 2) launch_one<8, 2>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
-    else launch_one<8, 3>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
-  } else if (qb == 4) {
-    launch_one<4, 4>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
-  } else if (qb == 2) {
-    launch_one<2, 4>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
-  } else {
-    launch_one<1, 4>(grid, lds, stream, qmean, kmean, vbs, out, nblk, heads, topk);
+  const int pairs = batch * heads;
+  const int chunk = route_pairs_per_chunk(batch, heads, nblk);
+  const int tiles = (nblk + kScoreTile - 1) / kScoreTile;
+  for (int bh0 = 0; bh0 < pairs; bh0 += chunk) {
+    const int g = pairs - bh0 < chunk ? pairs - bh0 : chunk;
+    hipLaunchKernelGGL(route_score_kernel, dim3((unsigned)(g * tiles * tiles)), dim3(kRouteThreads), 0,
+                       stream, qmean, kmean, vbs, scores, bh0, nblk, heads, tiles);
+    const int rows = g * nblk;
+    const dim3 sgrid((unsigned)((rows + kRouteWaves - 1) / kRouteWaves));
+    hipLaunchKernelGGL(route_select_kernel, sgrid, dim3(kRouteThreads), 0, stream, scores, out, bh0,
+                       rows, nblk, topk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace vsa

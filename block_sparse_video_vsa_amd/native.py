@@ -62,8 +62,9 @@ _SIGNATURES = {
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t,
                                          _c_void_p]),
+    "vsa_route_workspace_size": (_size_t, [_i32, _i32, _i32]),
     "vsa_route_topk": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
-                                      _i32, _i32, _c_void_p]),
+                                      _i32, _i32, _c_void_p, _size_t, _c_void_p]),
     "vsa_cube_count": (_size_t, [_i32, _i32, _i32]),
     "vsa_cube_vbs": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _size_t]),
     "vsa_tile": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -439,8 +440,17 @@ def vsa_fwd_proxy_bsr(q, k, v, sel_indptr, sel_indices, vbs, kmean, vsum, prefix
     return out
 
 
-def vsa_route_topk(qmean, kmean, vbs, topk: int, out=None):
-    """Top-k key blocks per query block by block-mean scores (C ABI vsa_route_topk)."""
+def route_workspace_size(batch: int, num_blocks: int, heads: int) -> int:
+    """Bytes of the fp64 score workspace vsa_route_topk needs (C ABI vsa_route_workspace_size)."""
+    return int(load_library().vsa_route_workspace_size(batch, num_blocks, heads))
+
+
+def vsa_route_topk(qmean, kmean, vbs, topk: int, out=None, workspace=None):
+    """Top-k key blocks per query block by block-mean scores (C ABI vsa_route_topk).
+
+    `workspace` (uint8, on the device) may be passed to reuse one allocation
+    across calls; it is allocated here otherwise.
+    """
     lib = load_library()
     dev = qmean.device
     B, nb, H, D = qmean.shape
@@ -450,6 +460,11 @@ def vsa_route_topk(qmean, kmean, vbs, topk: int, out=None):
     if out is None:
         out = torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
     _need(out, "topk_idx", torch.int32, dev, (B, H, nb, topk))
+    nbytes = route_workspace_size(B, nb, H)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     _check("vsa_route_topk", lib.vsa_route_topk(_ptr(qmean), _ptr(kmean), _ptr(vbs), _ptr(out), B, nb, H,
-                                                D, topk, _stream(dev)))
+                                                D, topk, _ptr(workspace), workspace.numel(),
+                                                _stream(dev)))
     return out

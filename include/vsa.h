@@ -284,14 +284,21 @@ vsa_status vsa_merge(const void* o1, const float* lse1, const void* o2, const fl
  *   topk_idx      int32 [batch, num_heads, num_blocks, topk] output: ready to
  *                 be the topk_idx of vsa_fwd.
  *   num_blocks    1 .. 7680; head_dim must be 128; 1 <= topk <= num_blocks.
+ *   workspace     device memory of at least vsa_route_workspace_size(batch,
+ *                 num_blocks, num_heads) bytes, 256-byte aligned
+ *                 (VSA_ERR_WORKSPACE / VSA_ERR_ALIGN otherwise): the fp64
+ *                 scores of as many (batch, head) pairs as fit about 256 MB
+ *                 (at least one pair, num_blocks^2 * 8 bytes); larger calls
+ *                 run in chunks of pairs.  Its contents on entry are ignored.
  *
- * Device memory, caller-owned, enqueued on `stream`; kmean must be 16-byte
- * aligned, qmean 2-byte, vbs and topk_idx 4-byte (VSA_ERR_ALIGN otherwise).
+ * Device memory, caller-owned, enqueued on `stream`; qmean and kmean must be
+ * 16-byte aligned, vbs and topk_idx 4-byte (VSA_ERR_ALIGN otherwise).
  */
+size_t vsa_route_workspace_size(int32_t batch, int32_t num_blocks, int32_t num_heads);
 vsa_status vsa_route_topk(const void* qmean, const void* kmean, const int32_t* vbs,
                           int32_t* topk_idx, int32_t batch, int32_t num_blocks,
                           int32_t num_heads, int32_t head_dim, int32_t topk,
-                          vsa_stream_t stream);
+                          void* workspace, size_t workspace_bytes, vsa_stream_t stream);
 
 /*
  * Cube tiling of a latent video grid ([SH]: 4 x 4 x 4 cubes of 64 tokens,

@@ -31,7 +31,8 @@ def test_every_declared_function_is_exported(lib):
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
             "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
-            "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk"} <= set(names)
+            "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk",
+            "vsa_route_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -200,12 +201,20 @@ def test_selection_format_helpers():
 
 
 def test_route_rejects_bad_arguments_on_host(lib):
+    need = lib.vsa_route_workspace_size(1, 624, 2)
+    assert need == 2 * 624 * 624 * 8                       # both pairs fit one chunk
+    assert lib.vsa_route_workspace_size(1, 7680, 40) == 7680 * 7680 * 8   # one pair per chunk
+    assert lib.vsa_route_workspace_size(1, 7681, 1) == 0
     r = lambda **kw: lib.vsa_route_topk(kw.get("q", FAKE), FAKE, FAKE, kw.get("o", FAKE), 1,
-                                        kw.get("nb", 624), 2, kw.get("D", 128), kw.get("k", 78), None)
+                                        kw.get("nb", 624), 2, kw.get("D", 128), kw.get("k", 78),
+                                        kw.get("ws", FAKE), kw.get("wsb", need), None)
     assert r(q=None) == NULL
     assert r(o=None) == NULL
     assert r(D=64) == UNSUP
     assert r(k=0) == SHAPE
     assert r(k=625) == SHAPE
     assert r(nb=7681, k=5) == SHAPE
-    assert r(q=FAKE + 1) == ALIGN
+    assert r(q=FAKE + 8) == ALIGN                          # means are read 16 bytes at a time
+    assert r(ws=None) == WS
+    assert r(wsb=need - 1) == WS
+    assert r(ws=FAKE + 16) == ALIGN

@@ -556,11 +556,12 @@ def test_route_topk_bitwise(dev, name, topk, heads):
 
 
 @pytest.mark.parametrize("nblk,heads,topks,kind", [
-    (200, 2, (1, 50, 200), "ties"),      # 8 query blocks per workgroup, ragged last group
+    (200, 2, (1, 50, 200), "ties"),      # ragged last score tile
+    (201, 3, (5, 201), "random"),        # odd block count: score rows start at odd offsets
     (200, 1, (7, 200), "zeros"),         # every score equal: pure index order
-    (1000, 1, (1, 125), "ties"),         # 4 per workgroup
-    (2000, 1, (250,), "random"),         # 2 per workgroup
-    (3200, 1, (3, 400), "random"),       # 1 per workgroup
+    (1000, 1, (1, 125), "ties"),
+    (2000, 1, (250,), "random"),
+    (3200, 1, (3, 400), "random"),
 ])
 def test_route_topk_ties_and_empty_blocks(dev, nblk, heads, topks, kind):
     """Synthetic block means with exact ties and empty blocks (vbs = 0): indices equal the oracle's."""
@@ -654,9 +655,9 @@ def test_side_stream_matches_default_stream(dev):
 
 
 def test_route_topk_at_the_block_limit(dev):
-    """7680 blocks (the largest routing shape: one score row per workgroup,
-    79 KB of LDS); sampled query rows against the oracle, which scores a row
-    from that row's mean and every key mean alone."""
+    """7680 blocks (the largest routing shape: one (batch, head) per chunk,
+    472 MB of fp64 scores); sampled query rows against the oracle, which
+    scores a row from that row's mean and every key mean alone."""
     rng = np.random.default_rng(28)
     nblk, topk = 7680, 40
     qm = W.f32_to_bf16_bits(rng.standard_normal((1, nblk, 1, 128)).astype(np.float32))
