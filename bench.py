@@ -46,23 +46,56 @@ def measured_traffic(config: str):
     workload or was taken on different kernel sources."""
     if config != "2" or not os.path.exists(TRAFFIC_FILE):
         return None
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
     fields = {}
     with open(TRAFFIC_FILE) as fh:
         for line in fh:
             if ":" in line:
                 k, _, v = line.partition(":")
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != h.hexdigest():
+    if fields.get("kernel_source_sha256") != _sources_digest():
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_config2_pipe_counters.txt")
+
+
+def _sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_counters(config: str):
+    """Pipeline counters of the attention kernel (MFMA busy, LDS bank-conflict
+    share, TA busy, clock under load) from the committed rocprofv3 --pmc summary,
+    or None when that summary is for another workload or other kernel sources."""
+    if config != "2" or not os.path.exists(COUNTERS_FILE):
+        return None
+    import re
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if m is None or m.group(1) != _sources_digest():
+        return None
+    pats = {"mfma_busy": r"MFMA pipe busy\s+([0-9.]+)",
+            "lds_bank_conflict_share": r"LDS bank-conflict share\s+([0-9.]+)",
+            "ta_busy": r"TA busy \(mean over TA units\)\s+([0-9.]+)",
+            "clock_ghz": r"shader clock under load\s+([0-9.]+) GHz",
+            "wave_wait_share": r"waves waiting \(s_waitcnt etc\.\)\s+([0-9.]+)"}
+    out = {}
+    for k, pat in pats.items():
+        mm = re.search(pat, text)
+        if mm is None:
+            return None
+        out[k] = float(mm.group(1))
+    out["source"] = os.path.relpath(COUNTERS_FILE, ROOT)
+    return out
 
 
 def cpu_baseline(wl, n_items: int, seed: int = 0) -> dict:
@@ -510,6 +543,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name),
                      "traffic_unit": "bytes per launch, HBM side (copy-calibrated FETCH_SIZE + WRITE_SIZE)"},
+        "counters": measured_counters(cfg.name),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
