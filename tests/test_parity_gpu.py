@@ -176,6 +176,66 @@ def test_dense_topk_all_cubes_and_batch(dev):
     assert g.ok(), str(g)
 
 
+def test_topk_at_the_table_limit(dev):
+    """topk = 4096, the most the tile table holds (8 bytes per entry in 32 KB of
+    LDS): one head of 4096 cubes in which every row selects every cube, each row
+    in its own random order, with ragged and empty cubes mixed in.  Sampled
+    items against the oracle; finiteness and zero padding rows everywhere."""
+    rng = np.random.default_rng(41)
+    B, H, nq = 1, 1, 4096
+    S = 64 * nq
+    q, k, v = (_rand_bf16(rng, (B, S, H, D)) for _ in range(3))
+    vbs = rng.choice(np.array([64, 64, 64, 48, 32, 17, 0], np.int32), size=nq).astype(np.int32)
+    topk = np.argsort(rng.random((B, H, nq, nq), dtype=np.float32), axis=-1).astype(np.int32)
+    scale = np.float32(1 / math.sqrt(D))
+    out = run_fwd(dev, q, k, v, topk, vbs, scale)
+    assert np.all(np.isfinite(O.bf16_to_f64(out))), "non-finite output"
+    assert pad_rows_zero(out, vbs)
+    pick = [0, nq - 1] + [int(np.nonzero(vbs == val)[0][0]) for val in (17, 32, 48)]
+    items = [(0, 0, c) for c in pick]
+    g_rows, ids = gather_rows(out, items, vbs)
+    r_rows = oracle_rows_fwd(q, k, v, topk, vbs, scale, items)
+    g = Grade(g_rows, r_rows, ids)
+    print(f"topk 4096 ({len(items)} sampled items): {g}")
+    assert g.ok(), str(g)
+
+
+def test_element_offsets_beyond_2_31(dev):
+    """Tensors of 2.7e9 elements (B=1, 4096 cubes, H=80): the last cubes and
+    heads sit past element 2^31, where 32-bit index arithmetic would wrap.  Only
+    the sampled items' query rows and the cubes they select hold data (the rest
+    is zero); those items are compared with the oracle, and the whole output is
+    checked for finiteness and zero padding rows."""
+    rng = np.random.default_rng(43)
+    B, H, nq = 1, 80, 4096
+    S = 64 * nq
+    assert B * S * H * D > 2 ** 31
+    vbs = np.full(nq, 64, np.int32)
+    vbs[nq - 1] = 40
+    vbs[nq - 2] = 0
+    base = np.arange(nq, dtype=np.int32)
+    topk = np.stack([base, (base + 1) % nq, (base + 3) % nq], axis=-1)
+    topk = np.broadcast_to(topk, (B, H, nq, 3)).copy()
+    q = np.zeros((B, S, H, D), np.uint16)
+    k = np.zeros((B, S, H, D), np.uint16)
+    v = np.zeros((B, S, H, D), np.uint16)
+    items = [(0, H - 1, nq - 1), (0, H - 1, nq - 3), (0, 0, nq - 1), (0, 41, 2047), (0, H - 1, 0)]
+    for _, h, qc in items:
+        q[0, 64 * qc:64 * qc + 64, h] = _rand_bf16(rng, (64, D))
+        for c in topk[0, h, qc]:
+            k[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
+            v[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
+    scale = np.float32(1 / math.sqrt(D))
+    out = run_fwd(dev, q, k, v, topk, vbs, scale)
+    assert not np.any((out & 0x7F80) == 0x7F80), "non-finite output"
+    assert pad_rows_zero(out, vbs)
+    g_rows, ids = gather_rows(out, items, vbs)
+    r_rows = oracle_rows_fwd(q, k, v, topk, vbs, scale, items)
+    g = Grade(g_rows, r_rows, ids)
+    print(f"2.7e9-element tensors ({len(items)} sampled items): {g}")
+    assert g.ok(), str(g)
+
+
 def test_topk_order_invariance_bitwise(dev):
     wl = W.generate("1")
     rng = np.random.default_rng(24)
