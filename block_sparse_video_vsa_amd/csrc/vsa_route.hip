@@ -105,6 +105,38 @@ __device__ __attribute__((always_inline)) inline int rank_in(const double* __res
   return rank;
 }
 
+// Value of lane ^ j (j = 1, 2, 4, 8, 16 or 32, a constant after unrolling),
+// exchanged inside the VALU: DPP quad permutes for 1 and 2, row rotations for
+// 4 and 8, the permlane swaps for 16 and 32 (no LDS round trip).
+__device__ __attribute__((always_inline)) inline unsigned xor_lane(unsigned v, int j, int lane) {
+  switch (j) {
+    case 1: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    case 2: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    case 4: {
+      const unsigned a = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);   // row_ror:4
+      const unsigned b = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, false);   // row_ror:12
+      return (lane & 4) ? a : b;
+    }
+    case 8: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror:8
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? r[0] : r[1];
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? r[0] : r[1];
+    }
+  }
+}
+__device__ __attribute__((always_inline)) inline uint64_t xor_lane64(uint64_t v, int j, int lane) {
+  const unsigned lo = xor_lane((unsigned)v, j, lane);
+  const unsigned hi = xor_lane((unsigned)(v >> 32), j, lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __attribute__((always_inline)) inline double xor_lane_f64(double v, int j, int lane) {
+  return __longlong_as_double((long long)xor_lane64((uint64_t)__double_as_longlong(v), j, lane));
+}
+
 // Sorts the listed candidates of one row into (score descending, index
 // ascending) order with a bitonic network over 64 * E positions, E per lane
 // (position E * lane + s in register s; positions past the list are padding
@@ -149,8 +181,8 @@ __device__ __attribute__((always_inline)) inline void sort_candidates(
         const bool lower = (lane & lm) == 0;
 #pragma unroll
         for (int s = 0; s < E; ++s) {
-          const double os = __shfl_xor(sv[s], lm, 64);
-          const int oi = __shfl_xor(iv[s], lm, 64);
+          const double os = xor_lane_f64(sv[s], lm, lane);
+          const int oi = (int)xor_lane((unsigned)iv[s], lm, lane);
           const bool asc = ((E * lane + s) & k) == 0;
           const bool keep_first = lower == asc;
           const bool mine_first = before(sv[s], iv[s], os, oi);
@@ -176,9 +208,7 @@ __device__ __attribute__((always_inline)) inline uint64_t wave_sort_desc(uint64_
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned lo = __shfl_xor((unsigned)v, j, 64);
-      const unsigned hi = __shfl_xor((unsigned)(v >> 32), j, 64);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      const uint64_t o = xor_lane64(v, j, lane);
       const bool lower = (lane & j) == 0;
       const bool desc = (lane & k) == 0;     // this block of the network puts the largest first
       const bool keep_larger = lower == desc;
@@ -228,8 +258,9 @@ __device__ __attribute__((always_inline)) inline void select_row(
   // eligible blocks (finite score) rank before every empty one
   int local = 0;
   chunks([&](int c) { local += val(c) != -INFINITY; });
-  int eligible = wave_inclusive_sum(local, lane);
-  eligible = __shfl(eligible, 63, 64);
+  int eligible = local;   // butterfly sum: every lane ends with the total
+#pragma unroll
+  for (int j = 1; j < 64; j <<= 1) eligible += (int)xor_lane((unsigned)eligible, j, lane);
   for (int t = eligible + lane; t < topk; t += 64) orow[t] = -1;
   int need = min(topk, eligible);
   if (need == 0) return;
