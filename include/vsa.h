@@ -290,6 +290,9 @@ vsa_status vsa_merge(const void* o1, const float* lse1, const void* o2, const fl
  *                 scores of as many (batch, head) pairs as fit about 256 MB
  *                 (at least one pair, num_blocks^2 * 8 bytes); larger calls
  *                 run in chunks of pairs.  Its contents on entry are ignored.
+ *                 vsa_route_workspace_size returns 0 for a shape the call
+ *                 rejects (batch, num_heads or num_blocks out of range, or
+ *                 batch * num_heads * num_blocks >= 2^31).
  *
  * Device memory, caller-owned, enqueued on `stream`; qmean and kmean must be
  * 16-byte aligned, vbs and topk_idx 4-byte (VSA_ERR_ALIGN otherwise).
