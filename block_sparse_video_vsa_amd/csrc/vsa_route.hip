@@ -105,38 +105,6 @@ __device__ __attribute__((always_inline)) inline int rank_in(const double* __res
   return rank;
 }
 
-// Value of lane ^ j (j = 1, 2, 4, 8, 16 or 32, a constant after unrolling),
-// exchanged inside the VALU: DPP quad permutes for 1 and 2, row rotations for
-// 4 and 8, the permlane swaps for 16 and 32 (no LDS round trip).
-__device__ __attribute__((always_inline)) inline unsigned xor_lane(unsigned v, int j, int lane) {
-  switch (j) {
-    case 1: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-    case 2: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-    case 4: {
-      const unsigned a = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);   // row_ror:4
-      const unsigned b = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, false);   // row_ror:12
-      return (lane & 4) ? a : b;
-    }
-    case 8: return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror:8
-    case 16: {
-      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-      return (lane & 16) ? r[0] : r[1];
-    }
-    default: {
-      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-      return (lane & 32) ? r[0] : r[1];
-    }
-  }
-}
-__device__ __attribute__((always_inline)) inline uint64_t xor_lane64(uint64_t v, int j, int lane) {
-  const unsigned lo = xor_lane((unsigned)v, j, lane);
-  const unsigned hi = xor_lane((unsigned)(v >> 32), j, lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __attribute__((always_inline)) inline double xor_lane_f64(double v, int j, int lane) {
-  return __longlong_as_double((long long)xor_lane64((uint64_t)__double_as_longlong(v), j, lane));
-}
-
 // Sorts the listed candidates of one row into (score descending, index
 // ascending) order with a bitonic network over 64 * E positions, E per lane
 // (position E * lane + s in register s; positions past the list are padding
