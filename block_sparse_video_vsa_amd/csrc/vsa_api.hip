@@ -16,6 +16,9 @@ namespace {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kMaxDynLds = 32 * 1024;   // beside the 32 KB of K/V tile buffers
 constexpr int64_t kMaxBlocks = (1 << 20) - 1;
+// (batch, head, block) triples: the V packing runs 256 threads on each, and a
+// launch stays at or below 2^31 threads.
+constexpr int64_t kMaxTriples = kMaxLaunchThreads / 256;
 constexpr int32_t kMaxRouteBlocks = 7680;    // one (batch, head) of scores: 472 MB of workspace
 constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stays below 2^32 bytes
 
@@ -60,7 +63,7 @@ vsa_status check_common(int32_t batch, int32_t seq_len, int32_t num_heads, int32
     return VSA_ERR_SHAPE;
   const int64_t nblk = seq_len / kBlock;
   if (nblk > kMaxBlocks) return VSA_ERR_SHAPE;
-  if ((int64_t)batch * num_heads * nblk > (int64_t)0x7FFFFFF0) return VSA_ERR_SHAPE;
+  if ((int64_t)batch * num_heads * nblk > kMaxTriples) return VSA_ERR_SHAPE;
   return VSA_OK;
 }
 
@@ -310,7 +313,8 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
   const int psplit = prefix_splits(nblk);
   const int pwidth = std::min<int>(kPrefixSplit, nblk);
   const int64_t items_per_bh = (int64_t)nprefix * psplit + nvideo;
-  if ((int64_t)batch * num_heads * items_per_bh > (int64_t)0x7FFFFFF0) return VSA_ERR_SHAPE;
+  // one 128-thread workgroup per work item, 8 * ceil(items / 8) of them
+  if ((int64_t)batch * num_heads * items_per_bh + 8 > kMaxLaunchThreads / 128) return VSA_ERR_SHAPE;
   const int table_cap = std::max(pwidth, nprefix + row_cap + nproxy);
   const int words = (nvideo + 31) / 32;
   // tile table of 8 bytes per entry; video items add a byte of weight per
@@ -455,8 +459,9 @@ vsa_status check_tile(const void* a, const void* b, int32_t batch, int32_t T, in
   if (!a || !b) return VSA_ERR_NULL;
   if (batch < 1 || num_heads < 1 || head_dim < 1 || cube_count(T, Hh, W) == 0) return VSA_ERR_SHAPE;
   if (((int64_t)num_heads * head_dim) % 8 != 0) return VSA_ERR_SHAPE;
+  // one 256-thread workgroup per row
   const int64_t rows = (int64_t)batch * kBlock * cube_count(T, Hh, W);
-  if (rows >= ((int64_t)1 << 31)) return VSA_ERR_SHAPE;
+  if (rows > kMaxLaunchThreads / 256) return VSA_ERR_SHAPE;
   if (!is_aligned(a, 16) || !is_aligned(b, 16)) return VSA_ERR_ALIGN;
   return VSA_OK;
 }

@@ -889,6 +889,7 @@ hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream)
   // about ten tiles of a typical item per sweep segment
   const int tiles = p.seg_tiles;
   p.nseg = std::min(kMaxSeg, std::max(1, (tiles + 5) / 10));
+  if (!launch_fits((int64_t)p.items_per_xcd * 8, kThreads)) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)p.items_per_xcd * 8u;
   if (proxy)
     hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, p);

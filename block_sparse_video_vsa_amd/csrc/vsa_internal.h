@@ -11,6 +11,12 @@ constexpr int kBlock = 64;       // tokens per cube / block
 constexpr int kHeadDim = 128;    // head geometry fixed at compile time
 constexpr int kTileBytes = kBlock * kHeadDim * 2;   // one 64 x 128 16-bit tile
 constexpr int kMaxSeg = 16;     // most sweep segments per item
+// Work-items of one launch: the dispatch packet holds 32 bits; launches stay
+// at or below 2^31 so that a grid never truncates or overflows.
+constexpr int64_t kMaxLaunchThreads = (int64_t)1 << 31;
+inline bool launch_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && blocks * threads <= kMaxLaunchThreads;
+}
 
 // ---- wavefront lane exchanges --------------------------------------------
 // Value of lane ^ j (j = 1, 2, 4, 8, 16 or 32, a constant after unrolling),

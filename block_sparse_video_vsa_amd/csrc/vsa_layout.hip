@@ -94,6 +94,7 @@ hipError_t launch_tile(const void* src, void* dst, int batch, int T, int Hh, int
   const int64_t rows_pad = (int64_t)kBlock * g.ct * g.ch * g.cw;
   const int64_t blocks = (int64_t)batch * (untile ? rows_nat : rows_pad);
   if (blocks == 0) return hipSuccess;
+  if (!launch_fits(blocks, kLayoutThreads)) return hipErrorInvalidValue;
   if (untile)
     hipLaunchKernelGGL(untile_kernel, dim3((unsigned)blocks), dim3(kLayoutThreads), 0, stream,
                        (const uint8_t*)src, (uint8_t*)dst, g, rows_nat, rows_pad, row_bytes);

@@ -123,6 +123,7 @@ hipError_t launch_prefix_merge(const float* part_o, const float* part_lse, const
                                uint16_t* out, int batch, int seq, int heads, int nprefix,
                                int psplit, hipStream_t stream) {
   const int64_t blocks = (int64_t)batch * heads * nprefix;
+  if (!launch_fits(blocks, 256)) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(prefix_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part_o,
                      part_lse, vbs, out, seq, heads, nprefix, psplit);

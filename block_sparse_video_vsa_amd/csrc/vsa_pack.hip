@@ -178,6 +178,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
 hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream) {
   const int64_t n = (int64_t)batch * p.heads * p.tiles;
   if (n <= 0) return hipSuccess;
+  if (!launch_fits(n, 256)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_vt_kernel, dim3((unsigned)n), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -187,6 +188,7 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              hipStream_t stream) {
   const int64_t n = (int64_t)batch * (seq / kBlock) * ((heads + 7) / 8);
   if (n <= 0) return hipSuccess;
+  if (!launch_fits(n, 256)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(preprocess_kernel, dim3((unsigned)n), dim3(256), 0, stream, k, v, vbs,
                      kmean, vsum, seq, heads);
   return hipGetLastError();

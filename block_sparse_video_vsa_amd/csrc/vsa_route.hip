@@ -44,6 +44,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace vsa {
 namespace {
 
@@ -438,6 +440,10 @@ int route_pairs_per_chunk(int batch, int heads, int nblk) {
   const size_t per_pair = (size_t)nblk * nblk * 8;
   const size_t cap = (size_t)256 << 20;   // score workspace target: 256 MB
   size_t g = cap / per_pair;
+  // launch sizes: score tiles^2 x 256 and selection nblk x 64 work-items per pair
+  const size_t tiles = (size_t)(nblk + kScoreTile - 1) / kScoreTile;
+  g = std::min(g, (size_t)kMaxLaunchThreads / (tiles * tiles * kRouteThreads));
+  g = std::min(g, (size_t)kMaxLaunchThreads / ((size_t)nblk * 64));
   if (g < 1) g = 1;
   const size_t pairs = (size_t)batch * heads;
   return (int)(g < pairs ? g : pairs);
@@ -455,6 +461,8 @@ hipError_t launch_route(const uint16_t* qmean, const uint16_t* kmean, const int3
   const int tiles = (nblk + kScoreTile - 1) / kScoreTile;
   for (int bh0 = 0; bh0 < pairs; bh0 += chunk) {
     const int g = pairs - bh0 < chunk ? pairs - bh0 : chunk;
+    if (!launch_fits((int64_t)g * tiles * tiles, kRouteThreads) || !launch_fits((int64_t)g * nblk, 64))
+      return hipErrorInvalidValue;
     hipLaunchKernelGGL(route_score_kernel, dim3((unsigned)(g * tiles * tiles)), dim3(kRouteThreads), 0,
                        stream, qmean, kmean, vbs, scores, bh0, nblk, heads, tiles);
     const int rows = g * nblk;

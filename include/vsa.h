@@ -34,12 +34,13 @@
  *     compile time, as in [RUN]).
  *   - Size limits (VSA_ERR_SHAPE otherwise): seq_len a positive multiple of 64
  *     with at most 2^20 - 1 cubes, 1 <= num_heads <= 65536, batch >= 1, and
- *     batch * num_heads * seq_len/64 < 2^31.  The per-workgroup tile table
- *     takes 8 bytes per entry out of 32 KB of LDS: topk <= 4096 for vsa_fwd;
- *     proxy calls need, for a video row, 8 bytes per possible tile (prefix
- *     blocks + row width + proxy tiles) plus 72 bytes per 64 video blocks
- *     within the same 32 KB, and batch * num_heads * (prefix blocks *
- *     ceil(seq_len/64 / 96) + video blocks) < 2^31.
+ *     batch * num_heads * seq_len/64 <= 2^23 (no launch exceeds 2^31 threads;
+ *     the V packing runs 256 threads per (batch, head, cube)).  The
+ *     per-workgroup tile table takes 8 bytes per entry out of 32 KB of LDS:
+ *     topk <= 4096 for vsa_fwd; proxy calls need, for a video row, 8 bytes per
+ *     possible tile (prefix blocks + row width + proxy tiles) plus 72 bytes per
+ *     64 video blocks within the same 32 KB, and batch * num_heads * (prefix
+ *     blocks * ceil(seq_len/64 / 96) + video blocks) <= 2^24 - 8 work items.
  */
 #ifndef VSA_H
 #define VSA_H
@@ -320,7 +321,9 @@ vsa_status vsa_route_topk(const void* qmean, const void* kmean, const int32_t* v
  * vsa_untile       the inverse gather: x_tiled -> x (padding rows are ignored).
  *
  * Elements are 16-bit (bf16 here, but the copy is bit-exact for any 2-byte
- * type); num_heads * head_dim must be a multiple of 8 (16-byte rows pieces) and
+ * type); batch * 64 * cubes <= 2^23 rows (VSA_ERR_SHAPE otherwise; one
+ * 256-thread workgroup per row); num_heads * head_dim must be a multiple of 8
+ * (16-byte rows pieces) and
  * both pointers 16-byte aligned (VSA_ERR_ALIGN otherwise).  Device memory,
  * caller-owned, enqueued on `stream`; x and x_tiled must not overlap.
  */

@@ -117,6 +117,20 @@ def test_stage_and_proxy_entry_points_reject_bad_arguments(lib):
     assert px(wsb=100) == WS
 
 
+def test_launch_size_limits_on_host(lib):
+    """Every launch stays at or below 2^31 threads: at most 2^23 (batch, head,
+    block) triples for the forward family and the block summaries, at most
+    2^24 - 8 proxy work items, at most 2^23 tiled rows."""
+    nb = (1 << 20) - 1
+    assert _fwd(lib, S=64 * nb, H=9) == SHAPE                       # 9 (2^20 - 1) > 2^23
+    assert lib.vsa_preprocess(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64 * nb, 9, 128, None) == SHAPE
+    # 50 000 prefix blocks, each split over ceil(100 000 / 96) key ranges: 5.2e7 items
+    assert lib.vsa_fwd_proxy(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64 * 100000,
+                             64 * 50000, 1, 128, 4, 0.1, FAKE, 1 << 30, None) == SHAPE
+    assert lib.vsa_tile(FAKE, FAKE, 2, 256, 256, 256, 2, 128, None) == SHAPE   # 2 x 64 x 64^3 rows
+    assert lib.vsa_untile(FAKE, FAKE, 2, 256, 256, 256, 2, 128, None) == SHAPE
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
