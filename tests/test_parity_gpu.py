@@ -540,6 +540,42 @@ def test_merge_against_the_oracle(dev):
 # --------------------------------------------------------------------------
 # bitmask and BSR selections for the proxy forward
 # --------------------------------------------------------------------------
+def test_proxy_at_the_table_limit(dev):
+    """Proxy forward with the largest selection rows its tile table holds: one
+    prefix block and 3500 video blocks, rows 3500 wide (8 bytes per possible
+    tile plus 72 bytes per 64 video blocks: 32 408 of the 32 768 bytes), each
+    row selecting 3000-3500 blocks so that the rest enter as proxy terms.  The
+    prefix row is split over 37 key ranges.  Block summaries bitwise, sampled
+    items against the oracle, finiteness and zero padding rows everywhere."""
+    rng = np.random.default_rng(47)
+    H, npb, nv = 1, 1, 3500
+    vbs = np.concatenate([[64], rng.choice(np.array([64, 64, 64, 40, 17, 0], np.int32), size=nv)]).astype(np.int32)
+    S = 64 * vbs.size
+    q, k, v = (_rand_bf16(rng, (1, S, H, D)) for _ in range(3))
+    sel = np.full((1, H, nv, nv), -1, np.int32)
+    for c in range(nv):
+        picks = rng.permutation(nv)[:int(rng.integers(3000, nv + 1))]
+        sel[0, 0, c, :picks.size] = picks
+    dq, dk, dv, dvbs = (to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True),
+                        to_dev(vbs, dev))
+    km, vs = vsa.vsa_preprocess(dk, dv, dvbs)
+    km_o, vs_o = O.vsa_preprocess(k, v, vbs)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(km), km_o) and np.array_equal(from_dev(vs), vs_o)
+    scale = np.float32(1 / math.sqrt(D))
+    out = from_dev(vsa.vsa_fwd_proxy(dq, dk, dv, to_dev(sel, dev), dvbs, km, vs, 64 * npb,
+                                     float(scale)))
+    assert np.all(np.isfinite(O.bf16_to_f64(out))), "non-finite output"
+    assert pad_rows_zero(out, vbs)
+    pick = [0, 1, vbs.size - 1] + [int(np.nonzero(vbs == val)[0][0]) for val in (17, 40)]
+    items = [(0, 0, c) for c in pick]
+    g_rows, ids = gather_rows(out, items, vbs)
+    r_rows = oracle_rows_proxy(q, k, v, sel, vbs, km_o, vs_o, 64 * npb, scale, items)
+    g = Grade(g_rows, r_rows, ids)
+    print(f"proxy at the table limit ({len(items)} sampled items): {g}")
+    assert g.ok(), str(g)
+
+
 def _proxy_formats(dev, wl_q, wl_k, wl_v, sel, vbs, prefix_len, scale, garbage_bits=False):
     """Outputs of the padded, bitmask and BSR calls (deterministic mode)."""
     nv = sel.shape[2]
