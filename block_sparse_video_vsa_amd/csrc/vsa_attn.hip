@@ -37,11 +37,12 @@
 // specialisation of the tile step, so the accumulators never cross
 // data-dependent control flow except the rescale.  Proxy and bf16 tiles follow.
 // The start block is the average sweep position of the workgroups running on
-// the same XCD (a per-XCD progress counter that every workgroup advances after
-// each segment), so the resident workgroups of a head move through its blocks
-// together and the XCD's L2 holds a narrow window of that head's K/V tiles
-// instead of all of them.  In deterministic mode the start depends only on the
-// workgroup index, so the order, and with it the rounding, is reproducible.
+// the same XCD (a per-XCD progress counter that every workgroup advances by a
+// segment's width as the segment begins), so the resident workgroups of a head
+// move through its blocks together and the XCD's L2 holds a narrow window of
+// that head's K/V tiles instead of all of them.  In deterministic mode the
+// start depends only on the workgroup index, so the order, and with it the
+// rounding, is reproducible.
 #include "vsa_internal.h"
 
 #include <math.h>
