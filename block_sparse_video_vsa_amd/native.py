@@ -156,16 +156,23 @@ def _default_scale(sm_scale):
     return 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
 
 
-# workspace cache: one buffer per (device, bytes), reused by later calls
+# Workspace cache: one buffer per (device, stream), reused by later calls of
+# the same size on that stream.  Calls on one stream run in order, so they may
+# share it; calls on different streams get different buffers (the library
+# requires that calls sharing a workspace do not overlap in time).  A buffer is
+# allocated while its stream is current, so the caching allocator orders its
+# reuse after the work queued on that stream.
 _ws_cache: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    key = (device, nbytes)
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
-    if ws is None:
+    if ws is None or ws.numel() != nbytes + 256:
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
-        _ws_cache.clear()
+        _ws_cache.pop(key, None)
+        while len(_ws_cache) >= 8:   # buffers of streams no longer in use
+            _ws_cache.pop(next(iter(_ws_cache)))
         _ws_cache[key] = ws
     off = (-ws.data_ptr()) % 256
     return ws[off:off + nbytes]
