@@ -131,6 +131,21 @@ def test_launch_size_limits_on_host(lib):
     assert lib.vsa_untile(FAKE, FAKE, 2, 256, 256, 256, 2, 128, None) == SHAPE
 
 
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No CPU fallback: with the shared library absent, every entry point of the
+    binding raises instead of computing anything."""
+    import torch
+    from block_sparse_video_vsa_amd import native
+    monkeypatch.setattr(native, "_lib", None)
+    monkeypatch.setattr(native, "LIB_PATH", str(tmp_path / "libvsa.so"))
+    with pytest.raises(ImportError):
+        native.load_library()
+    t = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ImportError):
+        native.vsa_fwd(t, t, t, torch.zeros((1, 1, 1, 1), dtype=torch.int32),
+                       torch.full((1,), 64, dtype=torch.int32))
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
