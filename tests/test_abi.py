@@ -234,6 +234,9 @@ def test_route_rejects_bad_arguments_on_host(lib):
     assert need == 2 * 624 * 624 * 8                       # both pairs fit one chunk
     assert lib.vsa_route_workspace_size(1, 7680, 40) == 7680 * 7680 * 8   # one pair per chunk
     assert lib.vsa_route_workspace_size(1, 7681, 1) == 0
+    # one block per row: a chunk is capped at 2^23 pairs, so that the score
+    # kernel's launch (one 256-thread workgroup per pair) stays at 2^31 threads
+    assert lib.vsa_route_workspace_size(4096, 1, 65536) == (1 << 23) * 8
     r = lambda **kw: lib.vsa_route_topk(kw.get("q", FAKE), FAKE, FAKE, kw.get("o", FAKE), 1,
                                         kw.get("nb", 624), 2, kw.get("D", 128), kw.get("k", 78),
                                         kw.get("ws", FAKE), kw.get("wsb", need), None)
