@@ -778,6 +778,24 @@ def test_side_stream_matches_default_stream(dev):
     assert np.array_equal(from_dev(out), ref)
 
 
+def test_route_topk_across_chunks(dev):
+    """1440 blocks: the fp64 score workspace holds 16 (batch, head) pairs, so
+    B = 2, H = 10 runs as two chunks (16 + 4 pairs, the boundary inside batch
+    1).  Sampled rows of every pair, bitwise against the oracle."""
+    rng = np.random.default_rng(29)
+    B, H, nblk, topk = 2, 10, 1440, 180
+    assert vsa.route_workspace_size(B, nblk, H) == 16 * nblk * nblk * 8
+    qm = W.f32_to_bf16_bits(rng.standard_normal((B, nblk, H, 128)).astype(np.float32))
+    km = W.f32_to_bf16_bits(rng.standard_normal((B, nblk, H, 128)).astype(np.float32))
+    vbs = rng.integers(0, 65, nblk).astype(np.int32)
+    got = vsa.vsa_route_topk(to_dev(qm, dev, True), to_dev(km, dev, True), to_dev(vbs, dev), topk)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    rows = np.array([0, 719, 1439])
+    want = O.route_topk(np.ascontiguousarray(qm[:, rows]), km, vbs, topk)
+    assert np.array_equal(got[:, :, rows], want)
+
+
 def test_route_topk_at_the_block_limit(dev):
     """7680 blocks (the largest routing shape: one (batch, head) per chunk,
     472 MB of fp64 scores); sampled query rows against the oracle, which
