@@ -200,12 +200,9 @@ def test_topk_at_the_table_limit(dev):
     assert g.ok(), str(g)
 
 
-def test_element_offsets_beyond_2_31(dev):
-    """Tensors of 2.7e9 elements (B=1, 4096 cubes, H=80): the last cubes and
-    heads sit past element 2^31, where 32-bit index arithmetic would wrap.  Only
-    the sampled items' query rows and the cubes they select hold data (the rest
-    is zero); those items are compared with the oracle, and the whole output is
-    checked for finiteness and zero padding rows."""
+def _offsets_case():
+    """B=1, 4096 cubes, H=80 (2.7e9 elements per tensor): only the sampled
+    items' query rows and the cubes they select hold data, the rest is zero."""
     rng = np.random.default_rng(43)
     B, H, nq = 1, 80, 4096
     S = 64 * nq
@@ -225,6 +222,15 @@ def test_element_offsets_beyond_2_31(dev):
         for c in topk[0, h, qc]:
             k[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
             v[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
+    return q, k, v, topk, vbs, items
+
+
+def test_element_offsets_beyond_2_31(dev):
+    """Tensors of 2.7e9 elements: the last cubes and heads sit past element
+    2^31, where 32-bit index arithmetic would wrap.  The sampled items are
+    compared with the oracle; the whole output is checked for finiteness and
+    zero padding rows."""
+    q, k, v, topk, vbs, items = _offsets_case()
     scale = np.float32(1 / math.sqrt(D))
     out = run_fwd(dev, q, k, v, topk, vbs, scale)
     assert not np.any((out & 0x7F80) == 0x7F80), "non-finite output"
@@ -234,6 +240,27 @@ def test_element_offsets_beyond_2_31(dev):
     g = Grade(g_rows, r_rows, ids)
     print(f"2.7e9-element tensors ({len(items)} sampled items): {g}")
     assert g.ok(), str(g)
+
+
+def test_lse_offsets_beyond_2_31(dev):
+    """The row log-sum-exp output at the same 2.7e9-element shape: sampled
+    rows against the oracle, -inf on padding rows and on the empty cube."""
+    q, k, v, topk, vbs, items = _offsets_case()
+    scale = np.float32(1 / math.sqrt(D))
+    out, lse = vsa.vsa_fwd_lse(to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True),
+                               to_dev(topk, dev), to_dev(vbs, dev), float(scale))
+    torch.cuda.synchronize()
+    del out
+    lse = lse.cpu().numpy()
+    worst = 0.0
+    for b, h, c in items:
+        _, l64 = O.vsa_fwd_lse_item(q, k, v, topk, vbs, scale, b, h, c)
+        n = l64.size
+        worst = max(worst, _lse_ok(lse[b, h, 64 * c:64 * c + n], l64))
+        assert np.all(np.isneginf(lse[b, h, 64 * c + n:64 * c + 64]))
+    nq = vbs.size
+    assert np.all(np.isneginf(lse[0, :, 64 * (nq - 2):64 * (nq - 1)]))   # the empty cube
+    print(f"2.7e9-element tensors: max |d lse| = {worst:.3g}")
 
 
 def test_topk_order_invariance_bitwise(dev):
