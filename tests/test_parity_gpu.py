@@ -263,6 +263,56 @@ def test_lse_offsets_beyond_2_31(dev):
     print(f"2.7e9-element tensors: max |d lse| = {worst:.3g}")
 
 
+def test_proxy_offsets_beyond_2_31(dev):
+    """Proxy forward on 2.7e9-element tensors (B=1, H=80, one prefix block and
+    4095 video blocks, three exact picks per row, every other video block a
+    proxy term).  Sampled rows, the last cube and head among them, hold data,
+    as do their exact blocks and the last 64-block proxy group; the rest is
+    zero.  Block summaries bitwise over the whole tensors, sampled items
+    against the oracle, finiteness and zero padding rows everywhere."""
+    rng = np.random.default_rng(53)
+    H, npb, nb = 80, 1, 4096
+    nv = nb - npb
+    S = 64 * nb
+    assert S * H * D > 2 ** 31
+    vbs = np.full(nb, 64, np.int32)
+    vbs[nb - 1] = 40
+    vbs[nb - 5] = 0
+    base = np.arange(nv, dtype=np.int32)
+    sel = np.stack([base, (base + 1) % nv, (base + 3) % nv, np.full(nv, -1, np.int32)], axis=-1)
+    sel = np.broadcast_to(sel, (1, H, nv, 4)).copy()
+    q = np.zeros((1, S, H, D), np.uint16)
+    k = np.zeros((1, S, H, D), np.uint16)
+    v = np.zeros((1, S, H, D), np.uint16)
+    items = [(0, H - 1, nb - 1), (0, H - 1, 0), (0, 0, nb - 2), (0, 41, 2048)]
+    for _, h, qb in items:
+        q[0, 64 * qb:64 * qb + 64, h] = _rand_bf16(rng, (64, D))
+        blocks = list(range(nb - 64, nb)) + [0]
+        if qb >= npb:
+            blocks += [npb + int(s) for s in sel[0, h, qb - npb] if s >= 0]
+        for c in blocks:
+            k[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
+            v[0, 64 * c:64 * c + 64, h] = _rand_bf16(rng, (64, D))
+    dq, dk, dv, dvbs = (to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True),
+                        to_dev(vbs, dev))
+    km, vs = vsa.vsa_preprocess(dk, dv, dvbs)
+    km_o, vs_o = O.vsa_preprocess(k, v, vbs)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(km), km_o) and np.array_equal(from_dev(vs), vs_o)
+    del km_o, vs_o
+    scale = np.float32(1 / math.sqrt(D))
+    out = from_dev(vsa.vsa_fwd_proxy(dq, dk, dv, to_dev(sel, dev), dvbs, km, vs, 64 * npb,
+                                     float(scale)))
+    km_h, vs_h = from_dev(km), from_dev(vs)
+    assert not np.any((out & 0x7F80) == 0x7F80), "non-finite output"
+    assert pad_rows_zero(out, vbs)
+    g_rows, ids = gather_rows(out, items, vbs)
+    r_rows = oracle_rows_proxy(q, k, v, sel, vbs, km_h, vs_h, 64 * npb, scale, items)
+    g = Grade(g_rows, r_rows, ids)
+    print(f"proxy, 2.7e9-element tensors ({len(items)} sampled items): {g}")
+    assert g.ok(), str(g)
+
+
 def test_topk_order_invariance_bitwise(dev):
     wl = W.generate("1")
     rng = np.random.default_rng(24)
