@@ -506,6 +506,34 @@ def test_cube_tile_untile_bitwise(dev, grid, B, H, D):
     assert np.array_equal(got.cpu().numpy().view(np.uint16), O.cube_untile(junk, *grid))
 
 
+def test_cube_tile_offsets_beyond_2_31(dev):
+    """Tile and untile of tensors past 2^31 elements (grid 15 x 63 x 254 -> 4096
+    cubes, 240 030 real rows, H = 80): the round trip is exact over the whole
+    tensor (compared on the GPU), padding rows are zero, and marked rows, the
+    last ones past element 2^31, land on the oracle's slots."""
+    T, Hh, Wd, H = 15, 63, 254, 80
+    slot, vbs = O.cube_layout(T, Hh, Wd)
+    n = T * Hh * Wd
+    S = 64 * vbs.size
+    assert n * H * D > 2 ** 31 and S * H * D > 2 ** 31
+    rng = np.random.default_rng(55)
+    rows = np.array([0, 1, n // 2, n - 2, n - 1])
+    marks = rng.integers(1, 2 ** 15, size=(rows.size, H, D)).astype(np.int16)
+    x = torch.zeros((1, n, H, D), dtype=torch.int16, device=dev)
+    x[0, torch.from_numpy(rows).to(dev)] = torch.from_numpy(marks).to(dev)
+    x[0, n - 300:n - 200] = torch.randint(-2 ** 15, 2 ** 15, (100, H, D), dtype=torch.int16, device=dev)
+    xt = vsa.vsa_tile(x, (T, Hh, Wd))
+    back = vsa.vsa_untile(xt, (T, Hh, Wd))
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    for r, m in zip(rows, marks):
+        assert np.array_equal(xt[0, int(slot[r])].cpu().numpy(), m)
+    used = torch.zeros(S, dtype=torch.bool, device=dev)
+    used[torch.from_numpy(slot).to(dev)] = True
+    assert not torch.any(xt[0, ~used])
+    assert int(slot[rows[-1]]) * H * D > 2 ** 31
+
+
 # --------------------------------------------------------------------------
 # row statistics and merge
 # --------------------------------------------------------------------------
