@@ -37,7 +37,7 @@
 // specialisation of the tile step, so the accumulators never cross
 // data-dependent control flow except the rescale.  Proxy and bf16 tiles follow.
 // The start block is the average sweep position of the workgroups running on
-// the same XCD (a per-XCD progress counter that every workgroup advances by a
+// the same XCD (per-XCD progress counters that every workgroup advances by a
 // segment's width as the segment begins), so the resident workgroups of a head
 // move through its blocks together and the XCD's L2 holds a narrow window of
 // that head's K/V tiles instead of all of them.  In deterministic mode the
@@ -96,10 +96,21 @@ __device__ inline int ent_group(int e) {
 // (wraps modulo 2^64).  Divided by the number of resident workgroups it is a
 // virtual clock that advances at their average sweep rate; a starting workgroup
 // begins its sweep at that position.  Only the tile order depends on it.  The
-// counter of XCD x is touched only by workgroups running there, which share
+// counters of XCD x are touched only by workgroups running there, which share
 // that XCD's L2, so workgroup-scope atomics and loads (served by the L2) are
 // enough; device scope would send every access past the L2.
-__device__ unsigned long long g_sweep_progress[8];
+// Each XCD's progress is split over kSweepSub counters kSweepStride elements
+// (4352 bytes) apart, so that they fall in different L2 channels: a workgroup
+// adds to the counter of its dispatch slot and a reader sums all of them.  With
+// one counter per XCD the atomics of its 128 resident workgroups serialise in
+// one channel and hold up every other access mapped to it.
+constexpr int kSweepSub = 8;
+constexpr int kSweepStride = 4352 / 8;
+__device__ unsigned long long g_sweep_progress[8 * kSweepSub * kSweepStride];
+
+__device__ inline unsigned long long* sweep_counter(int xcd, int sub) {
+  return &g_sweep_progress[(xcd * kSweepSub + sub) * kSweepStride];
+}
 
 // Softmax variants of a tile step.
 enum : int { kModeFull = 0, kModePad = 1, kModeProxy = 2, kModeAny = 3 };
@@ -188,10 +199,17 @@ __device__ inline void issue_k(const uint16_t* kbase, uint32_t row_bytes, int rm
   const uint32_t l0 = opaque_s(lds_addr(sk));
   if (!kMayClamp || r0 + 4 * N - 1 <= rmax) {
     const uint32_t kl = opaque_v(klane);
+    // The row addresses advance from the first one; row_bytes and the LDS
+    // start go through opaque values so that the per-copy products are not
+    // hoisted out of the tile loop, where they would hold about 40 SGPRs and
+    // be spilled to VGPR lanes and reloaded on every tile.
+    const uint32_t rs = opaque_s(row_bytes);
+    const char* kr = kb + (size_t)r0 * rs;
+    const uint32_t m0 = opaque_s(l0 + (uint32_t)r0 * 256u);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int rb = r0 + 4 * i;
-      dma16(kb + (size_t)rb * row_bytes, kl ^ (uint32_t)((rb & 15) << 4), l0 + rb * 256);
+      dma16(kr, kl ^ (uint32_t)(((r0 + 4 * i) & 15) << 4), m0 + 1024u * i);
+      kr += 4 * rs;
     }
   } else {
     const int pcx = (lane & 15) ^ (lane >> 4);
@@ -209,13 +227,12 @@ __device__ inline void issue_k(const uint16_t* kbase, uint32_t row_bytes, int rm
 // vlane = 16 * lane.
 template <int N>
 __device__ inline void issue_v(const uint8_t* vtile, int base, uint32_t vlane, unsigned char* sv) {
-  const uint32_t l0 = opaque_s(lds_addr(sv));
+  const uint32_t ob = opaque_s((uint32_t)base);   // not hoisted, as in issue_k
+  const uint32_t m0 = opaque_s(lds_addr(sv) + ob);
+  const uint8_t* vb = vtile + ob;
   const uint32_t vl = opaque_v(vlane);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int off = base + 1024 * i;
-    dma16(vtile + off, vl, l0 + off);
-  }
+  for (int i = 0; i < N; ++i) dma16(vb + 1024 * i, vl, m0 + 1024u * i);
 }
 
 // S^T (NKB x 32 keys, 32 queries) = K . Q^T.  Register i of s[kb] in lane
@@ -497,7 +514,7 @@ __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st
   const int nblk = x.p->nblk;
   for (int s = 0; s < nseg; ++s) {
     if (x.tid == 0 && !x.p->deterministic)
-      __hip_atomic_fetch_add(&g_sweep_progress[x.xcd],
+      __hip_atomic_fetch_add(sweep_counter(x.xcd, (int)((blockIdx.x >> 3) & (kSweepSub - 1))),
                              (unsigned long long)(seg_first(s + 1, nblk, nseg) - seg_first(s, nblk, nseg)),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGFull);
@@ -667,8 +684,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       sStart = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
     } else {
       // Start block: the average position of the XCD's resident workgroups.
-      const unsigned long long prog =
-          __hip_atomic_load(&g_sweep_progress[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      unsigned long long prog = 0;
+      for (int k = 0; k < kSweepSub; ++k)
+        prog += __hip_atomic_load(sweep_counter(xcd, k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       sStart = (int)((prog / (unsigned long long)p.sweep_slots) % (unsigned long long)p.nblk);
     }
   }
