@@ -453,6 +453,9 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   const int nv = ent_nv(e);
   const bool px = kProxy && (MODE == kModeProxy || (MODE == kModeAny && (e & kEntProxy)));
   const uint8_t* wts = kProxy ? x.wt + kBlock * ent_id(e) : nullptr;
+  // The running max, the probabilities and O += P V run at raised wave
+  // priority: where both waves of a SIMD can issue, this phase goes first.
+  __builtin_amdgcn_s_setprio(2);
   if (kCompute) {
     if (MODE == kModeAny) {
       if (px) tile_max<NKB, kModeProxy>(s, nv, wts, x.c, x.hh, st);
@@ -483,6 +486,7 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
       pv_half<BF16>(x.sv, kb, pk, x.ln, x.hh, st);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   wg_barrier();   // both waves are done with sV
   if (has_next) issue_tile_v<kProxy>(x, en);
 }
