@@ -59,7 +59,7 @@ __device__ __attribute__((always_inline)) inline double xor_lane_f64(double v, i
 // Elements are fp16 when the tile's values fit fp16 well, else bf16 (flag 1).
 // On gfx950 the PV operand reads of this layout (32 rows d, one chunk per
 // lane) meet LDS bank conflicts on about half of their cycles; the swizzle
-// (d / 4) % 4 removes them but measured slower, because the global-to-LDS
+// (d / 4) % 4 removes them but measured no faster, because the global-to-LDS
 // copies, not the LDS, set the attention kernel's pace.
 __host__ __device__ inline int vt_swizzle(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
 
