@@ -104,7 +104,7 @@ __device__ inline int ent_group(int e) {
 // adds to the counter of its dispatch slot and a reader sums all of them.  With
 // one counter per XCD the atomics of its 128 resident workgroups serialise in
 // one channel and hold up every other access mapped to it.
-constexpr int kSweepSub = 8;
+constexpr int kSweepSub = 4;
 constexpr int kSweepStride = 4352 / 8;
 __device__ unsigned long long g_sweep_progress[8 * kSweepSub * kSweepStride];
 

@@ -73,7 +73,7 @@ const char* vsa_status_string(vsa_status s);
 /*
  * Accumulation order.  The attention kernels visit each query cube's KV tiles
  * in an order chosen for L2 reuse.  By default that order follows the live
- * progress of the other workgroups on the same XCD (counters of 272 KB per
+ * progress of the other workgroups on the same XCD (counters of 136 KB per
  * device, held by the library), so two identical calls may differ in the last
  * bits of fp32 rounding, always within the documented accuracy.  With
  * deterministic mode on, the order depends only on the shapes and the inputs:
