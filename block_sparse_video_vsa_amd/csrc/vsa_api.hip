@@ -7,8 +7,6 @@
 
 #include <math.h>
 
-#include <atomic>
-
 using namespace vsa;
 
 namespace {
@@ -21,8 +19,6 @@ constexpr int64_t kMaxBlocks = (1 << 20) - 1;
 constexpr int64_t kMaxTriples = kMaxLaunchThreads / 256;
 constexpr int32_t kMaxRouteBlocks = 7680;    // one (batch, head) of scores: 472 MB of workspace
 constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stays below 2^32 bytes
-
-std::atomic<int> g_deterministic{0};
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -77,7 +73,6 @@ AttnParams base_params(int32_t batch, int32_t seq_len, int32_t num_heads, float 
   p.n_items = batch * num_heads * p.nblk;
   p.items_per_xcd = (p.n_items + 7) / 8;
   p.c = sm_scale * 1.4426950408889634f;   // log2(e): softmax evaluated with exp2
-  p.deterministic = g_deterministic.load(std::memory_order_relaxed);
   return p;
 }
 
@@ -95,14 +90,6 @@ extern "C" const char* vsa_status_string(vsa_status s) {
     case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale must be finite and >= 0";
   }
   return "VSA_ERR_UNKNOWN";
-}
-
-extern "C" void vsa_set_deterministic(int32_t enable) {
-  g_deterministic.store(enable ? 1 : 0, std::memory_order_relaxed);
-}
-
-extern "C" int32_t vsa_get_deterministic(void) {
-  return g_deterministic.load(std::memory_order_relaxed);
 }
 
 extern "C" size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
@@ -274,6 +261,26 @@ extern "C" vsa_status vsa_preprocess(const void* k, const void* v, const int32_t
                         (hipStream_t)stream) != hipSuccess)
     return VSA_ERR_LAUNCH;
   return VSA_OK;
+}
+
+extern "C" vsa_status vsa_kc_stats(const void* kmean, const int32_t* vbs, float* kc_mean,
+                                   float* kc_var_diag, int32_t batch, int32_t num_blocks,
+                                   int32_t num_heads, int32_t head_dim, int32_t first_block,
+                                   int32_t block_count, vsa_stream_t stream) {
+  if (!kmean || !vbs || !kc_mean || !kc_var_diag) return VSA_ERR_NULL;
+  if (head_dim != kHeadDim) return VSA_ERR_UNSUPPORTED;
+  if (batch < 1 || num_heads < 1 || num_heads > kMaxHeads || num_blocks < 1 ||
+      num_blocks > kMaxBlocks || first_block < 0 || block_count < 0 ||
+      (int64_t)first_block + block_count > num_blocks)
+    return VSA_ERR_SHAPE;
+  if ((int64_t)batch * num_heads * 256 > kMaxLaunchThreads) return VSA_ERR_SHAPE;
+  if (!is_aligned(kmean, 2) || !is_aligned(vbs, 4) || !is_aligned(kc_mean, 4) ||
+      !is_aligned(kc_var_diag, 4))
+    return VSA_ERR_ALIGN;
+  return launch_kc_stats((const uint16_t*)kmean, vbs, kc_mean, kc_var_diag, batch, num_blocks,
+                         num_heads, first_block, block_count, (hipStream_t)stream) == hipSuccess
+             ? VSA_OK
+             : VSA_ERR_LAUNCH;
 }
 
 namespace {

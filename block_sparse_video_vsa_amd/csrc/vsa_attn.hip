@@ -36,20 +36,15 @@
 // padding keys, half, half with padding keys), each kind through a straight-line
 // specialisation of the tile step, so the accumulators never cross
 // data-dependent control flow except the rescale.  Proxy and bf16 tiles follow.
-// The start block is the average sweep position of the workgroups running on
-// the same XCD (per-XCD progress counters that every workgroup advances by a
-// segment's width as the segment begins), so the resident workgroups of a head
-// move through its blocks together and the XCD's L2 holds a narrow window of
-// that head's K/V tiles instead of all of them.  In deterministic mode the
-// start depends only on the workgroup index, so the order, and with it the
-// rounding, is reproducible.
+// The start block follows from the workgroup's dispatch slot so that the
+// resident workgroups of a head move through its blocks together and the XCD's
+// L2 holds a narrow window of that head's K/V tiles instead of all of them; it
+// depends on nothing but the shapes, so every call gives the same bits.
 #include "vsa_internal.h"
 
 #include <math.h>
 
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 namespace vsa {
 namespace {
@@ -57,6 +52,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -69,6 +66,7 @@ constexpr int kThreads = 128;
 // many log2 units, so probabilities stay below 2^8 (well inside fp16's range)
 // while tiles whose maximum grew only a little skip the accumulator rescale.
 constexpr float kRescaleSlack = 8.0f;
+
 
 // Tile-table entry: block/tile id (bits 0-19), valid rows (20-26), bf16 V (27),
 // proxy tile (28).
@@ -90,26 +88,6 @@ __device__ inline int ent_group(int e) {
   if (nv > 32) return kGFullPad;
   if (nv == 32) return kGHalf;
   return kGHalfPad;
-}
-
-// Sweep progress per XCD, in blocks swept by all workgroups of all launches
-// (wraps modulo 2^64).  Divided by the number of resident workgroups it is a
-// virtual clock that advances at their average sweep rate; a starting workgroup
-// begins its sweep at that position.  Only the tile order depends on it.  The
-// counters of XCD x are touched only by workgroups running there, which share
-// that XCD's L2, so workgroup-scope atomics and loads (served by the L2) are
-// enough; device scope would send every access past the L2.
-// Each XCD's progress is split over kSweepSub counters kSweepStride elements
-// (4352 bytes) apart, so that they fall in different L2 channels: a workgroup
-// adds to the counter of its dispatch slot and a reader sums all of them.  With
-// one counter per XCD the atomics of its 128 resident workgroups serialise in
-// one channel and hold up every other access mapped to it.
-constexpr int kSweepSub = 4;
-constexpr int kSweepStride = 4352 / 8;
-__device__ unsigned long long g_sweep_progress[8 * kSweepSub * kSweepStride];
-
-__device__ inline unsigned long long* sweep_counter(int xcd, int sub) {
-  return &g_sweep_progress[(xcd * kSweepSub + sub) * kSweepStride];
 }
 
 // Softmax variants of a tile step.
@@ -164,23 +142,31 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline unsigned bf16_rne_bits(float f) {
-  const unsigned u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Low part of a probability pair in fp16: lo = fp16(p - hi) for the fp16 pair
+// hi = fp16(p), each difference formed exactly from the fp16 value and the fp32
+// probability by one mixed-precision fma and rounded once.  hi + lo carries p
+// to a relative 2^-22 (hi alone: 2^-12).
+__device__ inline unsigned f16_low_part(unsigned hi, float p0, float p1) {
+  unsigned lo;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(lo)
+      : "v"(hi), "v"(p0), "v"(p1));
+  return lo;
 }
 
-// Probabilities p0, p1 (fp32, >= 0) -> packed fp16 pair (round toward zero);
-// the row sum gets exactly the values the MFMA will multiply.
-__device__ inline unsigned pack_f16(float p0, float p1, float& lsum) {
-  const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-  lsum = __builtin_amdgcn_fdot2(h, (f16x2){(_Float16)1.0f, (_Float16)1.0f}, lsum, false);
-  return __builtin_bit_cast(unsigned, h);
-}
-// Same for bf16 tiles (round to nearest even).
-__device__ inline unsigned pack_bf16(float p0, float p1, float& lsum) {
-  const unsigned a = bf16_rne_bits(p0), b = bf16_rne_bits(p1);
-  lsum += __uint_as_float(a << 16) + __uint_as_float(b << 16);
-  return a | (b << 16);
+// Tiles whose values do not fit fp16 multiply bf16 V by a two-term bf16 split
+// of each probability, p = hi + lo with hi = bf16(p), lo = bf16(p - hi): 16
+// significant bits, so the pair carries p to a relative 2^-17 (fp16 alone:
+// 2^-12).  The row sum takes hi + lo, the values the two MFMAs multiply.
+__device__ inline void split_bf16(float p0, float p1, unsigned& hi, unsigned& lo, float& h0,
+                                  float& h1, float& l0, float& l1) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+  h0 = __uint_as_float(hi << 16);
+  h1 = __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+  l0 = __uint_as_float(lo << 16);
+  l1 = __uint_as_float(lo & 0xFFFF0000u);
 }
 
 // Issue the global->LDS copies of one tile's K rows: N instructions of four
@@ -325,64 +311,94 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
 // values the MFMA multiplies.  A proxy key stands for a whole block: its value
 // operand is the block's value total, so the numerator takes its probability
 // as is and only the denominator multiplies it by the block's valid-row count.
-template <int MODE, bool BF16>
+// fp16 tiles fill pk with fp16 probabilities and, with kSplitP, pl with their
+// fp16 low parts (hi + lo, see f16_low_part); bf16 tiles always fill pk with the
+// high and pl with the low bf16 parts.  The plain forward keeps single fp16
+// probabilities (relative 2^-12 each); the proxy forward splits them, because
+// its value totals and long prefix rows leave less margin to the bf16 rounding
+// of the outputs, at the cost of twice the O += P V products.
+template <int MODE, bool BF16, bool kSplitP>
 __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_t* wts, float c,
-                                  float nmc, int hh, float& lsum, unsigned (&pk)[8]) {
-  if (MODE == kModeProxy) {
-    auto keyw = [&](int i) { return proxy_weight(wts, kb, i, hh); };
-    auto prob = [&](int i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
-      return keyw(i) > 0.0f ? e : 0.0f;
-    };
-    if (BF16) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const unsigned a = bf16_rne_bits(prob(i)), b = bf16_rne_bits(prob(i + 1));
-        lsum = fmaf(__uint_as_float(a << 16), keyw(i), lsum);
-        lsum = fmaf(__uint_as_float(b << 16), keyw(i + 1), lsum);
-        pk[i / 2] = a | (b << 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(prob(i), prob(i + 1)));
-        const f16x2 wv = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(keyw(i), keyw(i + 1)));
-        lsum = __builtin_amdgcn_fdot2(h, wv, lsum, false);   // weights <= 64: exact in fp16
-        pk[i / 2] = __builtin_bit_cast(unsigned, h);
-      }
-    }
-    return;
-  }
+                                  float nmc, int hh, float& lsum, unsigned (&pk)[8],
+                                  unsigned (&pl)[8]) {
+  auto keyw = [&](int i) { return proxy_weight(wts, kb, i, hh); };
   auto prob = [&](int i) {
     const float e = __builtin_amdgcn_exp2f(fmaf(sk[i], c, nmc));
+    if (MODE == kModeProxy) return keyw(i) > 0.0f ? e : 0.0f;
     return (MODE == kModePad && key_of(kb, i, hh) >= nv) ? 0.0f : e;
   };
   if (BF16) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_bf16(prob(i), prob(i + 1), lsum);
+    for (int i = 0; i < 16; i += 2) {
+      float h0, h1, l0, l1;
+      split_bf16(prob(i), prob(i + 1), pk[i / 2], pl[i / 2], h0, h1, l0, l1);
+      if (MODE == kModeProxy) {
+        lsum = fmaf(h0 + l0, keyw(i), lsum);
+        lsum = fmaf(h1 + l1, keyw(i + 1), lsum);
+      } else {
+        lsum += (h0 + l0) + (h1 + l1);
+      }
+    }
   } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) pk[i / 2] = pack_f16(prob(i), prob(i + 1), lsum);
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = prob(i), p1 = prob(i + 1);
+      const f16x2 h = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+      // proxy weights <= 64 are exact in fp16
+      const f16x2 wv = MODE == kModeProxy
+                           ? __builtin_convertvector((f32x2){keyw(i), keyw(i + 1)}, f16x2)
+                           : one;
+      pk[i / 2] = __builtin_bit_cast(unsigned, h);
+      lsum = __builtin_amdgcn_fdot2(h, wv, lsum, false);
+      if (kSplitP) {
+        pl[i / 2] = f16_low_part(pk[i / 2], p0, p1);
+        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pl[i / 2]), wv, lsum, false);
+      }
+    }
   }
 }
 
 // O^T (128 d x 32 queries) += V^T . P^T for one 32-key half kb: 16-key steps
 // ks = 2kb, 2kb+1 with B operand pk[4(ks%2)..+3] (keys 16ks + 8(j/4) + 4hh + j%4);
 // the A operand is row d = 32db + ln of the packed V tile, chunk 2(ks%2) + hh.
-template <bool BF16>
-__device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8], int ln,
-                               int hh, State& st) {
+// bf16 tiles run each step twice, with the high and the low probability parts.
+template <bool BF16, bool kSplitP>
+__device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8],
+                               const unsigned (&pl)[8], int ln, int hh, State& st) {
   const int sw = ((ln >> 1) ^ (ln >> 3)) & 3;
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     const unsigned char* vb = sv + kb * 8192 + ln * 64 + (((k2 * 2 + hh) ^ sw) << 4);
     const u32x4 pb = {pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
     if (BF16) {
-      const bf16x8 bb = __builtin_bit_cast(bf16x8, pb);
-      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 0 * 2048), bb, st.o0, 0, 0, 0);
-      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 1 * 2048), bb, st.o1, 0, 0, 0);
-      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 2 * 2048), bb, st.o2, 0, 0, 0);
-      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vb + 3 * 2048), bb, st.o3, 0, 0, 0);
+      const u32x4 lb = {pl[4 * k2], pl[4 * k2 + 1], pl[4 * k2 + 2], pl[4 * k2 + 3]};
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, pb), bl = __builtin_bit_cast(bf16x8, lb);
+#define VSA_PV_BF16(acc, db)                                                          \
+      {                                                                               \
+        const bf16x8 a = *(const bf16x8*)(vb + (db) * 2048);                          \
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);           \
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);           \
+      }
+      VSA_PV_BF16(st.o0, 0)
+      VSA_PV_BF16(st.o1, 1)
+      VSA_PV_BF16(st.o2, 2)
+      VSA_PV_BF16(st.o3, 3)
+#undef VSA_PV_BF16
+    } else if (kSplitP) {
+      const u32x4 lb = {pl[4 * k2], pl[4 * k2 + 1], pl[4 * k2 + 2], pl[4 * k2 + 3]};
+      const f16x8 bh = __builtin_bit_cast(f16x8, pb), bl = __builtin_bit_cast(f16x8, lb);
+#define VSA_PV_F16(acc, db)                                                           \
+      {                                                                               \
+        const f16x8 a = *(const f16x8*)(vb + (db) * 2048);                            \
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh, acc, 0, 0, 0);            \
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl, acc, 0, 0, 0);            \
+      }
+      VSA_PV_F16(st.o0, 0)
+      VSA_PV_F16(st.o1, 1)
+      VSA_PV_F16(st.o2, 2)
+      VSA_PV_F16(st.o3, 3)
+#undef VSA_PV_F16
     } else {
       const f16x8 bb = __builtin_bit_cast(f16x8, pb);
       st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 2048), bb, st.o0, 0, 0, 0);
@@ -403,7 +419,7 @@ struct Ctx {
   int64_t bh_tiles;        // (b * heads + h) * nblk
   int64_t bh_proxy;        // (b * heads + h) * nproxy
   uint32_t row_bytes, klane, vlane;
-  int w, lane, ln, hh, tid, xcd;
+  int w, lane, ln, hh, tid;
   float c;
 };
 
@@ -476,14 +492,14 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
     const float nmc = -st.mc;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      unsigned pk[8];
+      unsigned pk[8], pl[8];
       if (MODE == kModeAny) {
-        if (px) half_probs<kModeProxy, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
-        else half_probs<kModePad, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
+        if (px) half_probs<kModeProxy, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        else half_probs<kModePad, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       } else {
-        half_probs<MODE, BF16>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk);
+        half_probs<MODE, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       }
-      pv_half<BF16>(x.sv, kb, pk, x.ln, x.hh, st);
+      pv_half<BF16, kProxy>(x.sv, kb, pk, pl, x.ln, x.hh, st);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -494,11 +510,9 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
 // Table cells: segment s, exact fp16 kind g -> 4 s + g; then proxy, bf16.
 __device__ inline int cell_proxy(int nseg) { return 4 * nseg; }
 __device__ inline int cell_bf16(int nseg) { return 4 * nseg + 1; }
-__device__ inline int seg_first(int s, int nblk, int nseg) { return (s * nblk + nseg - 1) / nseg; }
 
 // All tiles of one item in the order of `ord`; cbeg[c] is the first position of
-// cell c (cbeg[4 nseg + 2] = number of tiles).  As each segment begins, the
-// sweep progress counter of the XCD advances by the segment's width in blocks.
+// cell c (cbeg[4 nseg + 2] = number of tiles).
 template <bool kProxy, bool kCompute>
 __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st, const int* ord,
                                  const int* cbeg, int nseg, int n) {
@@ -515,12 +529,7 @@ __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st
       body(e, en, has_next);
     }
   };
-  const int nblk = x.p->nblk;
   for (int s = 0; s < nseg; ++s) {
-    if (x.tid == 0 && !x.p->deterministic)
-      __hip_atomic_fetch_add(sweep_counter(x.xcd, (int)((blockIdx.x >> 3) & (kSweepSub - 1))),
-                             (unsigned long long)(seg_first(s + 1, nblk, nseg) - seg_first(s, nblk, nseg)),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGFull);
     cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModePad, false>(x, qop, st, e, en, hn); }, 4 * s + kGFullPad);
     cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGHalf);
@@ -536,7 +545,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
   __shared__ int sCell[2 * (4 * kMaxSeg + 2) + 1];   // tiles per cell, then first position per cell
-  __shared__ int sStart;
   extern __shared__ int sDyn[];
 
   const int tid = threadIdx.x;
@@ -680,23 +688,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int ncell = 4 * nseg + 2;
   int* ccnt = sCell;                     // [ncell] tiles per cell
   int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
-  if (tid == 0) {
-    if (p.deterministic) {
-      // Start block from the dispatch slot (a fixed 128 slots per XCD, so the
-      // order depends on nothing but the shapes): resident workgroups spread
-      // over the blocks.
-      sStart = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
-    } else {
-      // Start block: the average position of the XCD's resident workgroups.
-      unsigned long long prog = 0;
-      for (int k = 0; k < kSweepSub; ++k)
-        prog += __hip_atomic_load(sweep_counter(xcd, k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      sStart = (int)((prog / (unsigned long long)p.sweep_slots) % (unsigned long long)p.nblk);
-    }
-  }
+  // Start block of the sweep, from the dispatch slot: workgroup i of an XCD
+  // starts about when workgroup i - 128 ends (128 are resident per XCD), and
+  // each finished sweep advances the average position of the resident ones by
+  // nblk / 128 blocks, so slot i joins them at i * nblk / 128.  The order
+  // depends on the shapes only, so results are reproducible bit for bit.
+  const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
   for (int t = tid; t < 2 * ncell + 1; t += kThreads) sCell[t] = 0;
   wg_barrier();
-  const int start = sStart;
   for (int t = tid; t < ncand; t += kThreads) {
     const int e = candidate(t);
     int k = 0x7FFFFFFF;
@@ -797,7 +796,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   x.ln = ln;
   x.hh = hh;
   x.tid = tid;
-  x.xcd = xcd;
   x.c = p.c;
   State st;
   st.o0 = f32x16{};
@@ -852,14 +850,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto store4 = [&](const f32x16& acc, int db) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      unsigned u[4];
+      float f[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = acc[4 * a + r] * inv;
-        if (!row_ok || !isfinite(v)) v = 0.0f;
-        u[r] = bf16_rne_bits(v);
+        const float v = acc[4 * a + r] * inv;
+        f[r] = (row_ok && isfinite(v)) ? v : 0.0f;
       }
-      *(u32x2*)(orow + 32 * db + 8 * a) = (u32x2){u[0] | (u[1] << 16), u[2] | (u[3] << 16)};
+      const unsigned u01 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){f[0], f[1]}, bf16x2));
+      const unsigned u23 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){f[2], f[3]}, bf16x2));
+      *(u32x2*)(orow + 32 * db + 8 * a) = (u32x2){u01, u23};
     }
   };
   store4(st.o0, 0);
@@ -878,37 +877,10 @@ size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
   return table > video ? table : video;
 }
 
-namespace {
-
-// Attention workgroups resident per XCD at once for this dynamic LDS size,
-// cached per (device, variant, LDS size).
-int resident_per_xcd(bool proxy, size_t dyn) {
-  struct Entry { int dev; bool proxy; size_t dyn; int slots; };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& e : cache)
-    if (e.dev == dev && e.proxy == proxy && e.dyn == dyn) return e.slots;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 8;
-  const hipError_t err = proxy
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<true>, kThreads, dyn)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<false>, kThreads, dyn);
-  if (err != hipSuccess) per_cu = 1;
-  const int slots = std::max(1, per_cu * cus / 8);
-  cache.push_back({dev, proxy, dyn, slots});
-  return slots;
-}
-
-}  // namespace
-
 hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream) {
   if (params.n_items <= 0) return hipSuccess;
   AttnParams p = params;
   const size_t dyn = attn_dyn_lds(p, proxy);
-  p.sweep_slots = resident_per_xcd(proxy, dyn);
   // about ten tiles of a typical item per sweep segment
   const int tiles = p.seg_tiles;
   p.nseg = std::min(kMaxSeg, std::max(1, (tiles + 5) / 10));

@@ -101,10 +101,8 @@ struct AttnParams {
   int n_items;              // batch * heads * items_per_bh
   int items_per_xcd;
   int table_cap;            // tile-table capacity (entries)
-  int sweep_slots;          // workgroups resident per XCD at once
   int nseg;                 // sweep segments per item (1..kMaxSeg)
   int seg_tiles;            // tiles of a typical item (sizes the segments)
-  int deterministic;        // 1: sweep start from the workgroup index only
   float c;                  // sm_scale * log2(e)
   // proxy prefix split (appended: the fields above keep their offsets)
   int items_per_bh;         // nblk, or (proxy) nprefix * psplit + nvideo
@@ -119,6 +117,11 @@ hipError_t launch_preprocess(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* kmean, uint16_t* vsum, int batch, int seq, int heads,
                              hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
+// Mean and population variance of the bf16 block key means over blocks
+// [first, first + count) with vbs > 0, per (batch, head, channel), fp32 out.
+hipError_t launch_kc_stats(const uint16_t* kc, const int32_t* vbs, float* mean, float* var,
+                           int batch, int nblk, int heads, int first, int count,
+                           hipStream_t stream);
 // Routing: top-k key blocks by block-mean scores.
 // Routing: top-k key blocks by block-mean scores, through an fp64 score
 // workspace that holds route_pairs_per_chunk (batch, head) pairs at a time.

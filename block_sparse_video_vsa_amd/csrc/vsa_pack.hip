@@ -2,6 +2,8 @@
 //   * pack_vt   -- rewrites each (batch, head, 64-row tile) of V (or of the
 //                  per-block value totals) as a key-major 16-bit tile laid out
 //                  exactly as the attention kernel's LDS wants it;
+//   * kc_stats   -- per (batch, head, channel) mean and variance of the block
+//                  key means (the Runner's KC statistics);
 //   * preprocess -- per-block key means and value totals (TensorRT-Edge-LLM
 //                  "Video Sparse Attention Runner", preprocess entry: BF16
 //                  [numBlocks, numHeads, 128] block means of K and block sums of V;
@@ -173,7 +175,68 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
   *(u32x4*)dst = out;
 }
 
+// Statistics of the block key means (Runner preprocess entry: FP32
+// [numHeads, 128] mean and diagonal variance of KC, with KC in its BF16
+// rounding).  One workgroup per (batch, head): thread t owns channel t % 128
+// and every second eligible block starting at first + t / 128; two passes
+// (mean, then the mean squared deviation) in float64, the halves combined in
+// LDS, each result rounded once from float64 to float32.
+__global__ __launch_bounds__(256) void kc_stats_kernel(const uint16_t* __restrict__ kc,
+                                                       const int32_t* __restrict__ vbs,
+                                                       float* __restrict__ mean_out,
+                                                       float* __restrict__ var_out, int nblk,
+                                                       int heads, int first, int count) {
+  __shared__ double part[2][kHeadDim];
+  __shared__ int npart[2];
+  const int tid = threadIdx.x;
+  const int d = tid & (kHeadDim - 1);
+  const int half = tid >> 7;
+  const int bh = blockIdx.x;
+  const int h = bh % heads;
+  const int b = bh / heads;
+  const uint16_t* col = kc + ((int64_t)b * nblk * heads + h) * kHeadDim + d;
+  const int64_t stride = (int64_t)heads * kHeadDim;
+  auto value = [&](int c) { return (double)__uint_as_float((unsigned)col[c * stride] << 16); };
+  double s = 0.0;
+  int n = 0;
+  for (int c = first + half; c < first + count; c += 2) {
+    if (vbs[c] <= 0) continue;
+    s += value(c);
+    ++n;
+  }
+  part[half][d] = s;
+  if (d == 0) npart[half] = n;
+  __syncthreads();
+  const int ntot = npart[0] + npart[1];
+  const double mean = ntot > 0 ? (part[0][d] + part[1][d]) / (double)ntot : 0.0;
+  __syncthreads();
+  double q = 0.0;
+  for (int c = first + half; c < first + count; c += 2) {
+    if (vbs[c] <= 0) continue;
+    const double e = value(c) - mean;
+    q += e * e;
+  }
+  part[half][d] = q;
+  __syncthreads();
+  if (half == 0) {
+    const double var = ntot > 0 ? (part[0][d] + part[1][d]) / (double)ntot : 0.0;
+    mean_out[(int64_t)bh * kHeadDim + d] = (float)mean;
+    var_out[(int64_t)bh * kHeadDim + d] = (float)var;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kc_stats(const uint16_t* kc, const int32_t* vbs, float* mean, float* var,
+                           int batch, int nblk, int heads, int first, int count,
+                           hipStream_t stream) {
+  const int64_t n = (int64_t)batch * heads;
+  if (n <= 0) return hipSuccess;
+  if (!launch_fits(n, 256)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kc_stats_kernel, dim3((unsigned)n), dim3(256), 0, stream, kc, vbs, mean,
+                     var, nblk, heads, first, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream) {
   const int64_t n = (int64_t)batch * p.heads * p.tiles;

@@ -8,7 +8,6 @@ call raises.
 """
 from __future__ import annotations
 
-import contextlib
 import ctypes
 import math
 import os
@@ -33,8 +32,6 @@ _f32 = ctypes.c_float
 # (name, restype, argtypes)
 _SIGNATURES = {
     "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "vsa_set_deterministic": (None, [_i32]),
-    "vsa_get_deterministic": (_i32, []),
     "vsa_fwd_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "vsa_fwd": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t, _c_void_p]),
@@ -62,6 +59,8 @@ _SIGNATURES = {
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t,
                                          _c_void_p]),
+    "vsa_kc_stats": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _c_void_p]),
     "vsa_route_workspace_size": (_size_t, [_i32, _i32, _i32]),
     "vsa_route_topk": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                       _i32, _i32, _c_void_p, _size_t, _c_void_p]),
@@ -102,26 +101,6 @@ def load_library() -> ctypes.CDLL:
 
 def status_string(status: int) -> str:
     return load_library().vsa_status_string(int(status)).decode()
-
-
-def set_deterministic(enable: bool) -> None:
-    """Process-wide accumulation-order switch (vsa_set_deterministic)."""
-    load_library().vsa_set_deterministic(1 if enable else 0)
-
-
-def get_deterministic() -> bool:
-    return bool(load_library().vsa_get_deterministic())
-
-
-@contextlib.contextmanager
-def deterministic(enable: bool = True):
-    """Run the enclosed calls with deterministic mode set to `enable`."""
-    prev = get_deterministic()
-    set_deterministic(enable)
-    try:
-        yield
-    finally:
-        set_deterministic(prev)
 
 
 def _check(fn: str, status: int) -> None:
@@ -265,6 +244,28 @@ def vsa_preprocess(k, v, vbs, kmean=None, vsum=None):
                             _stream(dev))
     _check("vsa_preprocess", st)
     return kmean, vsum
+
+
+def vsa_kc_stats(kmean, vbs, first_block: int, block_count: int, mean=None, var=None):
+    """Mean and population variance of the block key means (C ABI vsa_kc_stats).
+
+    kmean: bf16 [B, nblk, H, 128]; statistics over blocks [first_block,
+    first_block + block_count) with vbs > 0.  Returns (mean, var), float32 [B, H, 128].
+    """
+    lib = load_library()
+    dev = kmean.device
+    B, nb, H, D = kmean.shape
+    _need(kmean, "kmean", torch.bfloat16, dev)
+    _need(vbs, "vbs", torch.int32, dev, (nb,))
+    if mean is None:
+        mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if var is None:
+        var = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _need(mean, "kc_mean", torch.float32, dev, (B, H, D))
+    _need(var, "kc_var_diag", torch.float32, dev, (B, H, D))
+    _check("vsa_kc_stats", lib.vsa_kc_stats(_ptr(kmean), _ptr(vbs), _ptr(mean), _ptr(var), B, nb, H,
+                                            D, int(first_block), int(block_count), _stream(dev)))
+    return mean, var
 
 
 def vsa_fwd_proxy(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale=None, out=None,

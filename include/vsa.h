@@ -72,16 +72,11 @@ const char* vsa_status_string(vsa_status s);
 
 /*
  * Accumulation order.  The attention kernels visit each query cube's KV tiles
- * in an order chosen for L2 reuse.  By default that order follows the live
- * progress of the other workgroups on the same XCD (counters of 136 KB per
- * device, held by the library), so two identical calls may differ in the last
- * bits of fp32 rounding, always within the documented accuracy.  With
- * deterministic mode on, the order depends only on the shapes and the inputs:
- * repeated calls give bitwise identical outputs, at some speed cost.  The setting is process-wide,
- * thread-safe, and applies to calls made after it returns.
+ * in an order chosen for L2 reuse that depends only on the shapes: repeated
+ * calls with the same inputs give bitwise identical outputs, and the output
+ * does not depend on the order of the entries of an index row.  The library
+ * holds no mutable state between calls.
  */
-void vsa_set_deterministic(int32_t enable);
-int32_t vsa_get_deterministic(void);
 
 /*
  * Workspace bytes vsa_fwd needs for this shape (0 if the shape is invalid).
@@ -98,8 +93,8 @@ size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
  *                 rows 64c .. 64c+63 form cube c.
  *   topk_idx      int32 [batch, num_heads, seq_len/64, topk]: selected KV cubes
  *                 of each (batch, head, query cube), in any order (the kernel
- *                 sorts each row; in deterministic mode the output is bitwise
- *                 independent of the order).
+ *                 sorts each row, so the output is bitwise independent of the
+ *                 order).
  *   vbs           int32 [seq_len/64]: valid rows of each cube, shared by all
  *                 batches and heads; rows >= vbs[c] are padding on both the
  *                 query and the key side.
@@ -155,6 +150,32 @@ vsa_status vsa_preprocess(const void* k, const void* v, const int32_t* vbs,
                           int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
                           vsa_stream_t stream);
 
+/*
+ * vsa_kc_stats -- statistics of the block key means ([RUN] preprocess entry:
+ * FP32 [numHeads, 128] mean and diagonal variance of KC, KC taken in its BF16
+ * rounding).
+ *
+ *   kmean         bf16 [batch, num_blocks, num_heads, head_dim] block key means
+ *                 (as written by vsa_preprocess), 2-byte aligned.
+ *   vbs           int32 [num_blocks]; a block takes part when vbs > 0.
+ *   first_block, block_count
+ *                 the blocks c in [first_block, first_block + block_count) are
+ *                 the population (for the packed proxy layout: the video blocks,
+ *                 first_block = prefix_len / 64).
+ *   kc_mean, kc_var_diag
+ *                 float32 [batch, num_heads, head_dim] outputs, 4-byte aligned:
+ *                 mean = sum(x_c) / n, var = sum((x_c - mean)^2) / n over the n
+ *                 taking part (population variance), evaluated in float64 and
+ *                 rounded to float32; both 0 when n = 0.
+ *
+ * VSA_ERR_SHAPE for an empty or out-of-range block range or sizes outside the
+ * common limits; device memory, caller-owned, enqueued on `stream`.
+ */
+vsa_status vsa_kc_stats(const void* kmean, const int32_t* vbs, float* kc_mean,
+                        float* kc_var_diag, int32_t batch, int32_t num_blocks, int32_t num_heads,
+                        int32_t head_dim, int32_t first_block, int32_t block_count,
+                        vsa_stream_t stream);
+
 /* Workspace bytes vsa_fwd_proxy needs for this shape (0 if the shape is invalid):
  * the packed V and vsum tiles, and the partial results of the prefix query
  * blocks.  A prefix block attends to every key block, so it runs as
@@ -196,7 +217,7 @@ vsa_status vsa_fwd_proxy(const void* q, const void* k, const void* v,
 /*
  * The same proxy forward with the exact blocks named in the two formats of
  * [PX] (FlashInfer description, "Bitmask format"); both give bit-identical
- * results to vsa_fwd_proxy with the same selection in deterministic mode.
+ * results to vsa_fwd_proxy with the same selection.
  *
  *   sel_mask      uint32 [batch, num_heads, nvideo, ceil(nvideo/32)], one row of
  *                 words per (batch, head, video query block): bit (c % 32) of

@@ -15,6 +15,9 @@ What it computes, and where the pages define it:
     preprocess entry: KC and VC are BF16 [numBlocks, numHeads, 128] block means
     of K and block sums of V; TensorRT-LLM VisualGen VSA review snippet: the
     mean divides the block sum by the valid count and casts to the input dtype.
+  * kc_stats -- the Runner's preprocess entry: FP32 [numHeads, 128] statistics
+    of KC (a mean and a diagonal variance per head and channel), with KC taken
+    in its BF16 rounding.
   * vsa_fwd_proxy -- the Runner's class description: in a packed
     [prefix | video] sequence the prefix queries see all keys exactly, while a
     64-row video query block sees the prefix, its neighbours and its chosen
@@ -42,7 +45,7 @@ BLOCK = 64
 __all__ = ["bf16_to_f64", "f64_to_bf16", "vsa_fwd", "vsa_fwd_item", "vsa_preprocess",
            "vsa_fwd_proxy", "vsa_fwd_proxy_item", "item_key_slots", "cube_layout", "cube_tile",
            "cube_untile", "vsa_fwd_lse_item", "vsa_fwd_lse", "merge_partials", "block_scores",
-           "route_topk"]
+           "route_topk", "kc_stats"]
 
 
 # --------------------------------------------------------------------------
@@ -87,12 +90,28 @@ def f64_to_bf16(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # the plain definition, one (batch, head, query block) at a time
 # --------------------------------------------------------------------------
+TINY = np.finfo(np.float64).tiny
+
+
+def _exp_weights(x: np.ndarray) -> np.ndarray:
+    """exp(x) for x <= 0, with results below the smallest normal float64 set to 0.
+
+    Each row holds a 1 (its maximum), so a dropped term is under 2.3e-308 of the
+    row's sum: far below float64 rounding of that sum, and no bf16-rounded
+    output can change.  Subnormal weights would only slow the matrix products
+    that follow by an order of magnitude.
+    """
+    e = np.exp(x)
+    e[e < TINY] = 0.0
+    return e
+
+
 def _softmax_attend(qm: np.ndarray, km: np.ndarray, vm: np.ndarray, scale: float,
                     return_weights: bool = False):
     """Textbook softmax attention in float64: rows of qm over the rows of km/vm."""
     s = (qm @ km.T) * scale
     m = s.max(axis=1, keepdims=True)
-    w = np.exp(s - m)
+    w = _exp_weights(s - m)
     w /= w.sum(axis=1, keepdims=True)
     o = w @ vm
     return (o, w) if return_weights else (o, None)
@@ -219,11 +238,11 @@ def vsa_fwd_proxy_item(q, k, v, sel_idx, vbs, kmean, vsum, prefix_len, sm_scale,
         m = np.maximum(s.max(axis=1, keepdims=True), t.max(axis=1, keepdims=True))
     else:
         m = s.max(axis=1, keepdims=True) if s.size else np.zeros((nq, 1))
-    es = np.exp(s - m)
+    es = _exp_weights(s - m)
     num = es @ vm
     den = es.sum(axis=1, keepdims=True)
     if proxy_blocks:
-        et = np.exp(t - m)
+        et = _exp_weights(t - m)
         num = num + et @ pv
         den = den + et @ wt[:, None]
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
@@ -310,7 +329,7 @@ def vsa_fwd_lse_item(q, k, v, topk_idx, vbs, sm_scale, b: int, h: int, qc: int):
     vm = bf16_to_f64(v[b, slots, h, :])
     s = (qm @ km.T) * float(np.float32(sm_scale))
     m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
+    e = _exp_weights(s - m)
     tot = e.sum(axis=1)
     return (e @ vm) / tot[:, None], m[:, 0] + np.log(tot)
 
@@ -395,3 +414,28 @@ def route_topk(qmean, kmean, vbs, topk: int):
                 pick = cand[order[:topk]]
                 out[b, h, i, :pick.size] = pick
     return out
+
+
+# --------------------------------------------------------------------------
+# statistics of the block key means (KC)
+# --------------------------------------------------------------------------
+def kc_stats(kmean, vbs, first_block: int, count: int):
+    """Per (batch, head, channel) mean and variance of the bf16 block key means.
+
+    Over the blocks c in [first_block, first_block + count) that hold keys
+    (vbs[c] > 0): mean = sum(x_c) / n and var = sum((x_c - mean)^2) / n, the
+    diagonal of the population covariance, both evaluated in float64 from the
+    bf16 values widened exactly and then rounded to float32 (nearest even).
+    kmean is bf16 bits [B, nblk, H, D]; returns two float32 arrays [B, H, D].
+    With no such block both statistics are 0.
+    """
+    B, _, H, D = kmean.shape
+    vbs = np.asarray(vbs)
+    blocks = [c for c in range(first_block, first_block + count) if vbs[c] > 0]
+    mean = np.zeros((B, H, D))
+    var = np.zeros((B, H, D))
+    if blocks:
+        x = bf16_to_f64(kmean[:, blocks])                  # [B, n, H, D]
+        mean = x.mean(axis=1)
+        var = ((x - mean[:, None]) ** 2).mean(axis=1)
+    return mean.astype(np.float32), var.astype(np.float32)

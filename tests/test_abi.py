@@ -29,26 +29,13 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"vsa_fwd", "vsa_preprocess", "vsa_fwd_proxy", "vsa_status_string",
             "vsa_fwd_workspace_size", "vsa_fwd_proxy_workspace_size", "vsa_pack_values",
-            "vsa_fwd_prepacked", "vsa_set_deterministic", "vsa_get_deterministic",
+            "vsa_fwd_prepacked",
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
             "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk",
-            "vsa_route_workspace_size"} <= set(names)
+            "vsa_route_workspace_size", "vsa_kc_stats"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
-
-
-def test_deterministic_switch(lib):
-    assert native.get_deterministic() is False
-    with native.deterministic():
-        assert lib.vsa_get_deterministic() == 1
-        with native.deterministic(False):
-            assert native.get_deterministic() is False
-        assert native.get_deterministic() is True
-    assert lib.vsa_get_deterministic() == 0
-    lib.vsa_set_deterministic(7)          # any non-zero value turns it on
-    assert lib.vsa_get_deterministic() == 1
-    lib.vsa_set_deterministic(0)
 
 
 def test_status_strings(lib):
@@ -115,6 +102,20 @@ def test_stage_and_proxy_entry_points_reject_bad_arguments(lib):
     assert px(sel=15) == SHAPE
     assert px(scale=-2.0) == VALUE
     assert px(wsb=100) == WS
+
+
+def test_kc_stats_rejects_bad_arguments_on_host(lib):
+    kc = lambda **kw: lib.vsa_kc_stats(  # noqa: E731
+        kw.get("km", FAKE), FAKE, kw.get("mean", FAKE), FAKE, 1, kw.get("nb", 16), 2,
+        kw.get("D", 128), kw.get("first", 4), kw.get("count", 12), None)
+    assert kc(km=None) == NULL
+    assert kc(mean=None) == NULL
+    assert kc(D=64) == UNSUP
+    assert kc(first=-1) == SHAPE
+    assert kc(count=13) == SHAPE            # 4 + 13 > 16 blocks
+    assert kc(nb=0) == SHAPE
+    assert kc(km=FAKE + 1) == ALIGN
+    assert kc(mean=FAKE + 2) == ALIGN
 
 
 def test_launch_size_limits_on_host(lib):

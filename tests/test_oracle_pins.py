@@ -96,6 +96,30 @@ def test_dense_equals_bruteforce_python_loops():
         assert np.allclose(o[0, i, 0], ref, rtol=0, atol=1e-12)
 
 
+def test_widely_spread_logits_equal_bruteforce():
+    """Logits spread over thousands of units (weights from 1 down to far below
+    the smallest normal float64): the oracle equals the pure-Python textbook
+    sum, whose math.exp keeps every sub-normal term, to 1e-12."""
+    rng = np.random.default_rng(5)
+    q, k, v, vbs, topk = _dense_inputs(rng, 2, 1)
+    # sm_scale 20: logit spread ~ 20 * |q||k| ~ 2500, so exp(s - max) spans the
+    # whole float64 range and many weights are sub-normal or zero
+    scale = np.float32(20.0)
+    o = O.vsa_fwd(q, k, v, topk, vbs, scale)
+    qf, kf, vf = (_f(x)[0, :, 0, :].tolist() for x in (q, k, v))
+    sc = float(scale)
+    tiny_seen = False
+    for i in (0, 9, 63, 64, 100, 127):
+        logits = [sc * sum(a * b for a, b in zip(qf[i], kf[j])) for j in range(128)]
+        mx = max(logits)
+        e = [math.exp(s - mx) for s in logits]
+        tiny_seen |= any(0.0 < x < 2.3e-308 for x in e)
+        z = sum(e)
+        ref = [sum(e[j] * vf[j][d] for j in range(128)) / z for d in range(D)]
+        assert np.allclose(o[0, i, 0], ref, rtol=0, atol=1e-12)
+    assert tiny_seen
+
+
 def test_dense_equals_torch_sdpa_float64():
     rng = np.random.default_rng(2)
     q, k, v, vbs, topk = _dense_inputs(rng, 8, 2, B=2)
@@ -530,3 +554,44 @@ def test_block_scores_round_after_each_term_in_d_order():
     assert s[0, 0] == 0.0
     assert s[1, 0] == 1.0
     assert s[2, 0] == 1.0 + 2.0 ** -30
+
+
+# ---------------------------------------------------------------- KC statistics
+def test_kc_stats_against_exact_fractions():
+    """Mean and population variance of the bf16 block means over the blocks
+    that hold keys, computed with exact rational arithmetic and rounded once to
+    float32: bitwise equal (a dropped block, the n - 1 divisor or a block with
+    vbs = 0 counted in fails)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(61)
+    B, nb, H = 2, 13, 3
+    km = _bf16(rng, (B, nb, H, D), 3.0)
+    vbs = rng.choice(np.array([64, 40, 0, 17], np.int32), size=nb).astype(np.int32)
+    first, count = 2, 10
+    mean, var = O.kc_stats(km, vbs, first, count)
+    xs = _f(km)
+    blocks = [c for c in range(first, first + count) if vbs[c] > 0]
+    assert 0 < len(blocks) < count
+    for b in range(B):
+        for h in range(H):
+            for d in (0, 5, 77, 127):
+                vals = [Fraction(float(xs[b, c, h, d])) for c in blocks]
+                m = sum(vals) / len(vals)
+                v = sum((x - m) ** 2 for x in vals) / len(vals)
+                assert mean[b, h, d] == np.float32(float(m))
+                assert var[b, h, d] == np.float32(float(v))
+
+
+def test_kc_stats_closed_forms():
+    B, nb, H = 1, 6, 2
+    km = np.zeros((B, nb, H, D), np.uint16)
+    vbs = np.full(nb, 64, np.int32)
+    km[:, :, 0, :] = 0x4040                 # 3.0 everywhere in head 0: variance 0
+    km[:, 0::2, 1, :] = 0x3F80              # head 1: 1.0 and -1.0 alternating
+    km[:, 1::2, 1, :] = 0xBF80
+    mean, var = O.kc_stats(km, vbs, 0, nb)
+    assert np.all(mean[0, 0] == 3.0) and np.all(var[0, 0] == 0.0)
+    assert np.all(mean[0, 1] == 0.0) and np.all(var[0, 1] == 1.0)
+    vbs[:] = 0                              # no block holds keys
+    mean, var = O.kc_stats(km, vbs, 0, nb)
+    assert not mean.any() and not var.any()
