@@ -75,11 +75,19 @@ constexpr int kEntBf16 = 1 << 27;
 constexpr int kEntProxy = 1 << 28;
 __device__ inline int ent_id(int e) { return e & 0xFFFFF; }
 __device__ inline int ent_nv(int e) { return (e >> kEntNvShift) & 127; }
-// Half tiles (exact fp16 tiles with vbs <= 32) load and multiply 32 keys only.
-__device__ inline bool ent_half(int e) { return !(e & (kEntBf16 | kEntProxy)) && ent_nv(e) <= 32; }
+// Tile sizes: exact fp16 tiles load and multiply only the key rows their vbs
+// needs, in granules of 16: 64 (full), 32 (half) or 16 (quarter) keys.  bf16
+// and proxy tiles are always full.
+enum : int { kTsFull = 0, kTsHalf = 1, kTsQuarter = 2 };
+__device__ inline int ent_size(int e) {
+  if (e & (kEntBf16 | kEntProxy)) return kTsFull;
+  const int nv = ent_nv(e);
+  return nv > 32 ? kTsFull : nv > 16 ? kTsHalf : kTsQuarter;
+}
 
-// Tile kinds, processed in this order.
-enum : int { kGFull = 0, kGFullPad, kGHalf, kGHalfPad, kGProxy, kGBf16, kGroups };
+// Tile kinds, processed in this order within a sweep segment (the first
+// kKinds), then proxy and bf16 tiles.
+enum : int { kGFull = 0, kGFullPad, kGHalf, kGHalfPad, kGQuarter, kKinds, kGProxy = kKinds, kGBf16 };
 __device__ inline int ent_group(int e) {
   if (e & kEntBf16) return kGBf16;
   if (e & kEntProxy) return kGProxy;
@@ -87,7 +95,8 @@ __device__ inline int ent_group(int e) {
   if (nv == 64) return kGFull;
   if (nv > 32) return kGFullPad;
   if (nv == 32) return kGHalf;
-  return kGHalfPad;
+  if (nv > 16) return kGHalfPad;
+  return kGQuarter;
 }
 
 // Softmax variants of a tile step.
@@ -268,7 +277,9 @@ __device__ inline float proxy_weight(const uint8_t* wts, int kb, int i, int hh) 
 // Running-max update for one tile: the tile's largest logit (scaled, log2
 // units), and a rescale of O and the row sum when it exceeds the running max
 // by more than kRescaleSlack.
-template <int NKB, int MODE>
+// NI registers of each 32-key half take part: 16, or 8 (keys 0-15) for
+// quarter tiles, whose keys 16-31 are not loaded.
+template <int NKB, int NI, int MODE>
 __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts, float c, int hh,
                                 State& st) {
   float t = -INFINITY;
@@ -277,20 +288,20 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < NI; ++i)
         t = fmaxf(t, fmaf(s[kb][i], c, __log2f(proxy_weight(wts, kb, i, hh))));
     t = pair_max(t);
   } else if (MODE == kModePad) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t = fmaxf(t, key_of(kb, i, hh) < nv ? s[kb][i] : -INFINITY);
+      for (int i = 0; i < NI; ++i) t = fmaxf(t, key_of(kb, i, hh) < nv ? s[kb][i] : -INFINITY);
     t = pair_max(t) * c;
   } else {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t = fmaxf(t, s[kb][i]);
+      for (int i = 0; i < NI; ++i) t = fmaxf(t, s[kb][i]);
     t = pair_max(t) * c;
   }
   const bool trig = t > st.mc + kRescaleSlack;
@@ -317,7 +328,7 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
 // probabilities (relative 2^-12 each); the proxy forward splits them, because
 // its value totals and long prefix rows leave less margin to the bf16 rounding
 // of the outputs, at the cost of twice the O += P V products.
-template <int MODE, bool BF16, bool kSplitP>
+template <int MODE, bool BF16, bool kSplitP, int NI>
 __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_t* wts, float c,
                                   float nmc, int hh, float& lsum, unsigned (&pk)[8],
                                   unsigned (&pl)[8]) {
@@ -329,7 +340,7 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
   };
   if (BF16) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 0; i < NI; i += 2) {
       float h0, h1, l0, l1;
       split_bf16(prob(i), prob(i + 1), pk[i / 2], pl[i / 2], h0, h1, l0, l1);
       if (MODE == kModeProxy) {
@@ -342,7 +353,7 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
   } else {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 0; i < NI; i += 2) {
       const float p0 = prob(i), p1 = prob(i + 1);
       const f16x2 h = __builtin_convertvector((f32x2){p0, p1}, f16x2);
       // proxy weights <= 64 are exact in fp16
@@ -360,23 +371,24 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
 }
 
 // O^T (128 d x 32 queries) += V^T . P^T for one 32-key half kb: 16-key steps
-// ks = 2kb, 2kb+1 with B operand pk[4(ks%2)..+3] (keys 16ks + 8(j/4) + 4hh + j%4);
-// the A operand is row d = 32db + ln of the packed V tile, chunk 2(ks%2) + hh.
+// ks = 2kb, 2kb+1 (only the first for quarter tiles, NK2 = 1) with B operand
+// pk[4(ks%2)..+3] (keys 16ks + 8(j/4) + 4hh + j%4); the A operand is row
+// d = 32db + ln of 16-key group ks of the packed V tile, chunk hh.
 // bf16 tiles run each step twice, with the high and the low probability parts.
-template <bool BF16, bool kSplitP>
+template <bool BF16, bool kSplitP, int NK2>
 __device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8],
                                const unsigned (&pl)[8], int ln, int hh, State& st) {
-  const int sw = ((ln >> 1) ^ (ln >> 3)) & 3;
+  const int chunk = (hh ^ vt_swizzle(ln)) << 4;
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const unsigned char* vb = sv + kb * 8192 + ln * 64 + (((k2 * 2 + hh) ^ sw) << 4);
+  for (int k2 = 0; k2 < NK2; ++k2) {
+    const unsigned char* vb = sv + kb * 8192 + k2 * 4096 + ln * 32 + chunk;
     const u32x4 pb = {pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
     if (BF16) {
       const u32x4 lb = {pl[4 * k2], pl[4 * k2 + 1], pl[4 * k2 + 2], pl[4 * k2 + 3]};
       const bf16x8 bh = __builtin_bit_cast(bf16x8, pb), bl = __builtin_bit_cast(bf16x8, lb);
 #define VSA_PV_BF16(acc, db)                                                          \
       {                                                                               \
-        const bf16x8 a = *(const bf16x8*)(vb + (db) * 2048);                          \
+        const bf16x8 a = *(const bf16x8*)(vb + (db) * 1024);                          \
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);           \
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);           \
       }
@@ -390,7 +402,7 @@ __device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (
       const f16x8 bh = __builtin_bit_cast(f16x8, pb), bl = __builtin_bit_cast(f16x8, lb);
 #define VSA_PV_F16(acc, db)                                                           \
       {                                                                               \
-        const f16x8 a = *(const f16x8*)(vb + (db) * 2048);                            \
+        const f16x8 a = *(const f16x8*)(vb + (db) * 1024);                            \
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh, acc, 0, 0, 0);            \
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl, acc, 0, 0, 0);            \
       }
@@ -401,10 +413,10 @@ __device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (
 #undef VSA_PV_F16
     } else {
       const f16x8 bb = __builtin_bit_cast(f16x8, pb);
-      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 2048), bb, st.o0, 0, 0, 0);
-      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 2048), bb, st.o1, 0, 0, 0);
-      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 2048), bb, st.o2, 0, 0, 0);
-      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 2048), bb, st.o3, 0, 0, 0);
+      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 1024), bb, st.o0, 0, 0, 0);
+      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 1024), bb, st.o1, 0, 0, 0);
+      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 1024), bb, st.o2, 0, 0, 0);
+      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 1024), bb, st.o3, 0, 0, 0);
     }
   }
 }
@@ -436,8 +448,11 @@ __device__ inline void issue_tile_k(const Ctx& x, int e) {
   } else {
     base = p.k + (((int64_t)x.b * p.seq + (int64_t)ent_id(e) * kBlock) * p.heads + x.h) * kHeadDim;
   }
-  if (ent_half(e)) issue_k<4, kProxy>(base, x.row_bytes, rmax, 16 * x.w, x.klane, x.lane, x.sk);
-  else issue_k<8, kProxy>(base, x.row_bytes, rmax, 32 * x.w, x.klane, x.lane, x.sk);
+  switch (ent_size(e)) {
+    case kTsFull: issue_k<8, kProxy>(base, x.row_bytes, rmax, 32 * x.w, x.klane, x.lane, x.sk); break;
+    case kTsHalf: issue_k<4, kProxy>(base, x.row_bytes, rmax, 16 * x.w, x.klane, x.lane, x.sk); break;
+    default: issue_k<2, kProxy>(base, x.row_bytes, rmax, 8 * x.w, x.klane, x.lane, x.sk); break;
+  }
 }
 
 template <bool kProxy>
@@ -446,20 +461,26 @@ __device__ inline void issue_tile_v(const Ctx& x, int e) {
   const uint8_t* base = (kProxy && (e & kEntProxy))
                             ? p.pt + (x.bh_proxy + ent_id(e)) * kTileBytes
                             : p.vt + (x.bh_tiles + ent_id(e)) * kTileBytes;
-  if (ent_half(e)) issue_v<4>(base, 4096 * x.w, x.vlane, x.sv);
-  else issue_v<8>(base, 8192 * x.w, x.vlane, x.sv);
+  switch (ent_size(e)) {
+    case kTsFull: issue_v<8>(base, 8192 * x.w, x.vlane, x.sv); break;
+    case kTsHalf: issue_v<4>(base, 4096 * x.w, x.vlane, x.sv); break;
+    default: issue_v<2>(base, 2048 * x.w, x.vlane, x.sv); break;
+  }
 }
 
 // One tile: wait for its K rows, S = K Q^T, release K and prefetch the next
 // tile's K rows, running max, wait for its V, probabilities and O += P V,
 // release V and prefetch the next tile's V.  NKB / MODE / BF16 are fixed per
 // tile kind (MODE kModeAny: bf16 tiles, exact or proxy, decided per tile).
-template <bool kProxy, bool kCompute, int NKB, int MODE, bool BF16>
+template <bool kProxy, bool kCompute, int TS, int MODE, bool BF16>
 __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st, int e, int en,
                                  bool has_next) {
-  // K(j) has landed once only V(j)'s copies (4 or 8 instructions per wave) are
-  // still in flight.
-  if (NKB == 1) wait_vmcnt<4>(); else wait_vmcnt<8>();
+  constexpr int NKB = TS == kTsFull ? 2 : 1;       // 32-key halves of S
+  constexpr int NI = TS == kTsQuarter ? 8 : 16;    // registers per half that hold loaded keys
+  constexpr int NK2 = TS == kTsQuarter ? 1 : 2;    // 16-key steps of O += P V per half
+  // K(j) has landed once only V(j)'s copies (8, 4 or 2 instructions per wave)
+  // are still in flight.
+  wait_vmcnt<(8 >> TS)>();
   wg_barrier();
   f32x16 s[2];
   if (kCompute) s_tile<NKB>(x.sk, qop, x.ln, x.hh, s);
@@ -474,16 +495,20 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   __builtin_amdgcn_s_setprio(2);
   if (kCompute) {
     if (MODE == kModeAny) {
-      if (px) tile_max<NKB, kModeProxy>(s, nv, wts, x.c, x.hh, st);
-      else tile_max<NKB, kModePad>(s, nv, wts, x.c, x.hh, st);
+      if (px) tile_max<NKB, NI, kModeProxy>(s, nv, wts, x.c, x.hh, st);
+      else tile_max<NKB, NI, kModePad>(s, nv, wts, x.c, x.hh, st);
     } else {
-      tile_max<NKB, MODE>(s, nv, wts, x.c, x.hh, st);
+      tile_max<NKB, NI, MODE>(s, nv, wts, x.c, x.hh, st);
     }
   }
 
   // V(j) has landed once only K(j+1)'s copies may still be in flight.
   if (has_next) {
-    if (ent_half(en)) wait_vmcnt<4>(); else wait_vmcnt<8>();
+    switch (ent_size(en)) {
+      case kTsFull: wait_vmcnt<8>(); break;
+      case kTsHalf: wait_vmcnt<4>(); break;
+      default: wait_vmcnt<2>(); break;
+    }
   } else {
     wait_vmcnt<0>();
   }
@@ -494,12 +519,12 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
     for (int kb = 0; kb < NKB; ++kb) {
       unsigned pk[8], pl[8];
       if (MODE == kModeAny) {
-        if (px) half_probs<kModeProxy, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
-        else half_probs<kModePad, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        if (px) half_probs<kModeProxy, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        else half_probs<kModePad, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       } else {
-        half_probs<MODE, BF16, kProxy>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        half_probs<MODE, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       }
-      pv_half<BF16, kProxy>(x.sv, kb, pk, pl, x.ln, x.hh, st);
+      pv_half<BF16, kProxy, NK2>(x.sv, kb, pk, pl, x.ln, x.hh, st);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -507,12 +532,12 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   if (has_next) issue_tile_v<kProxy>(x, en);
 }
 
-// Table cells: segment s, exact fp16 kind g -> 4 s + g; then proxy, bf16.
-__device__ inline int cell_proxy(int nseg) { return 4 * nseg; }
-__device__ inline int cell_bf16(int nseg) { return 4 * nseg + 1; }
+// Table cells: segment s, exact fp16 kind g -> kKinds s + g; then proxy, bf16.
+__device__ inline int cell_proxy(int nseg) { return kKinds * nseg; }
+__device__ inline int cell_bf16(int nseg) { return kKinds * nseg + 1; }
 
 // All tiles of one item in the order of `ord`; cbeg[c] is the first position of
-// cell c (cbeg[4 nseg + 2] = number of tiles).
+// cell c (cbeg[kKinds nseg + 2] = number of tiles).
 template <bool kProxy, bool kCompute>
 __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st, const int* ord,
                                  const int* cbeg, int nseg, int n) {
@@ -530,21 +555,23 @@ __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st
     }
   };
   for (int s = 0; s < nseg; ++s) {
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGFull);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModePad, false>(x, qop, st, e, en, hn); }, 4 * s + kGFullPad);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModeFull, false>(x, qop, st, e, en, hn); }, 4 * s + kGHalf);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 1, kModePad, false>(x, qop, st, e, en, hn); }, 4 * s + kGHalfPad);
+    const int c0 = kKinds * s;
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeFull, false>(x, qop, st, e, en, hn); }, c0 + kGFull);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGFullPad);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsHalf, kModeFull, false>(x, qop, st, e, en, hn); }, c0 + kGHalf);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsHalf, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGHalfPad);
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsQuarter, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGQuarter);
   }
   if (kProxy)
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeProxy, false>(x, qop, st, e, en, hn); }, cell_proxy(nseg));
-  cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, 2, kModeAny, true>(x, qop, st, e, en, hn); }, cell_bf16(nseg));
+    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeProxy, false>(x, qop, st, e, en, hn); }, cell_proxy(nseg));
+  cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeAny, true>(x, qop, st, e, en, hn); }, cell_bf16(nseg));
 }
 
 template <bool kProxy>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
-  __shared__ int sCell[2 * (4 * kMaxSeg + 2) + 1];   // tiles per cell, then first position per cell
+  __shared__ int sCell[2 * (kKinds * kMaxSeg + 2) + 1];   // tiles per cell, then first position per cell
   extern __shared__ int sDyn[];
 
   const int tid = threadIdx.x;
@@ -685,7 +712,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     return blk | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + blk] ? kEntBf16 : 0);
   };
   const int nseg = p.nseg;
-  const int ncell = 4 * nseg + 2;
+  const int ncell = kKinds * nseg + 2;
   int* ccnt = sCell;                     // [ncell] tiles per cell
   int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
   // Start block of the sweep, from the dispatch slot: workgroup i of an XCD
@@ -701,9 +728,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int k = 0x7FFFFFFF;
     if (e >= 0) {
       const int g = ent_group(e);
-      if (g <= kGHalfPad) {
+      if (g < kKinds) {
         const int rel = ent_id(e) - start + (ent_id(e) < start ? p.nblk : 0);
-        k = ((4 * (rel * nseg / p.nblk) + g) << 20) | rel;
+        k = ((kKinds * (rel * nseg / p.nblk) + g) << 20) | rel;
       } else {
         k = ((g == kGProxy ? cell_proxy(nseg) : cell_bf16(nseg)) << 20) | ent_id(e);
       }

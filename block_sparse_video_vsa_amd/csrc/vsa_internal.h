@@ -53,15 +53,16 @@ __device__ __attribute__((always_inline)) inline double xor_lane_f64(double v, i
 
 // ---- packed V tiles ------------------------------------------------------
 // Each (batch, head, tile) V^T tile is 16 KB: two 8 KB key halves (keys 0-31,
-// 32-63); inside a half, 128 rows (one per head-dim index d) of 32 keys = 64 B,
-// split in four 16 B chunks that are XOR-swizzled by vt_swizzle(d); inside a
-// chunk the eight keys follow the MFMA k-slot order (see vsa_attn.hip).
+// 32-63), each of two 4 KB 16-key groups; inside a group, 128 rows (one per
+// head-dim index d) of 16 keys = 32 B, split in two 16 B chunks (the two lane
+// halves of the MFMA operand) stored in the order given by vt_swizzle(d);
+// inside a chunk the eight keys follow the MFMA k-slot order (see
+// vsa_attn.hip).  A tile's first 16, 32 or 64 keys are thus its first 4, 8 or
+// 16 KB.  The swizzle puts rows d and d + 8 of a 16-row band in different
+// 16-byte bank groups, so the operand reads (16 consecutive rows per group of
+// lanes) touch every LDS bank once.
 // Elements are fp16 when the tile's values fit fp16 well, else bf16 (flag 1).
-// On gfx950 the PV operand reads of this layout (32 rows d, one chunk per
-// lane) meet LDS bank conflicts on about half of their cycles; the swizzle
-// (d / 4) % 4 removes them but measured no faster, because the global-to-LDS
-// copies, not the LDS, set the attention kernel's pace.
-__host__ __device__ inline int vt_swizzle(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+__host__ __device__ inline int vt_swizzle(int d) { return (d >> 3) & 1; }
 
 struct PackParams {
   const uint16_t* src;      // bf16 BSHD source rows

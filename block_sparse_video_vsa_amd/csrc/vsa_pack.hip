@@ -25,12 +25,11 @@ __device__ inline unsigned bf16_to_f16_bits(unsigned x) {
 
 // One workgroup (256 threads) packs one 64 x 128 tile.
 //
-// Output layout (16 KB): key half kh (keys 0-31 / 32-63) at kh * 8192; inside a
-// half, row d (0..127) at d * 64; row d holds four 16-byte chunks, logical
-// chunk c stored at physical slot c ^ vt_swizzle(d).  Logical chunk c = 2*g + s
-// covers the 16-key group g (keys 16g..16g+15 of the half) and lane half s of
-// the MFMA operand; its eight elements are keys
-//   16g + 8*(j/4) + 4*s + (j%4),  j = 0..7,
+// Output layout (16 KB): key half kh (keys 0-31 / 32-63) at kh * 8192, its
+// 16-key group g at + g * 4096; inside a group, row d (0..127) at d * 32 holds
+// two 16-byte chunks, chunk s (the MFMA operand's lane half) at physical slot
+// s ^ vt_swizzle(d).  Its eight elements are keys
+//   32 kh + 16 g + 8*(j/4) + 4*s + (j%4),  j = 0..7,
 // the k-slot order in which the 32x32 MFMA output leaves the probabilities.
 // Padding keys (rows >= the tile's valid count) are written as zeros, so a
 // zero probability never meets a NaN or Inf pad value.
@@ -81,13 +80,11 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(PackParams p) {
   uint8_t* dst = p.dst + (int64_t)id * kTileBytes;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int o = tid + 256 * it;
+    const int o = tid + 256 * it;   // 16-byte chunk o of the output tile
     const int kh = o >> 9;
-    const int rem = o & 511;
-    const int d = rem >> 2;
-    const int c = (rem & 3) ^ vt_swizzle(d);
-    const int g = c >> 1;
-    const int s = c & 1;
+    const int g = (o >> 8) & 1;
+    const int d = (o >> 1) & 127;
+    const int s = (o & 1) ^ vt_swizzle(d);
     unsigned e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
