@@ -4,6 +4,7 @@
 #include "vsa_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 #include <math.h>
 
@@ -88,6 +89,8 @@ extern "C" const char* vsa_status_string(vsa_status s) {
     case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE: workspace missing or too small";
     case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale must be finite and >= 0";
+    case VSA_ERR_SCRATCH:
+      return "VSA_ERR_SCRATCH: the shape needs more scratch than the fixed buffer of vsa_fwd_noalloc";
   }
   return "VSA_ERR_UNKNOWN";
 }
@@ -189,6 +192,56 @@ extern "C" vsa_status vsa_fwd(const void* q, const void* k, const void* v,
   if (st != VSA_OK) return st;
   return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
                         workspace, s);
+}
+
+// ---- forward without allocation ------------------------------------------
+// The scratch of vsa_fwd_noalloc: one fixed array per GPU, held by the loaded
+// library until the process ends.  Host code reaches it only through the
+// device address hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current; nullptr if the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t vsa_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" vsa_status vsa_fwd_noalloc(const void* q, const void* k, const void* v,
+                                      const int32_t* topk_idx, const int32_t* vbs, void* out,
+                                      int32_t batch, int32_t seq_len, int32_t num_heads,
+                                      int32_t head_dim, int32_t topk, float sm_scale,
+                                      vsa_stream_t stream) {
+  // shape checks first (with a stand-in workspace size), then the scratch limit
+  vsa_status st = check_fwd(q, k, v, topk_idx, vbs, out, batch, seq_len, num_heads, head_dim,
+                            topk, sm_scale, (void*)kWsAlign, (size_t)-1, true, true);
+  if (st != VSA_OK) return st;
+  if (ws_layout(batch, num_heads, seq_len / kBlock, 0).total > kScratchBytes) return VSA_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (ws == nullptr) return VSA_ERR_LAUNCH;
+  hipStream_t s = (hipStream_t)stream;
+  st = enqueue_pack(v, vbs, batch, seq_len, num_heads, ws, s);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale, ws, s);
 }
 
 extern "C" vsa_status vsa_fwd_lse(const void* q, const void* k, const void* v,

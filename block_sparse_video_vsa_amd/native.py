@@ -35,6 +35,9 @@ _SIGNATURES = {
     "vsa_fwd_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "vsa_fwd": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+    "vsa_fwd_noalloc_max_bytes": (_size_t, []),
+    "vsa_fwd_noalloc": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p]),
     "vsa_pack_values": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p,
                                        _size_t, _c_void_p]),
     "vsa_fwd_prepacked": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -192,6 +195,26 @@ def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale=None, out=None, workspace=None):
                      topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
                      workspace.numel(), _stream(dev))
     _check("vsa_fwd", st)
+    return out
+
+
+def vsa_fwd_noalloc(q, k, v, topk_idx, vbs, out, sm_scale=None):
+    """vsa_fwd through the C ABI's allocation-free entry point (vsa_fwd_noalloc).
+
+    `out` (bf16 [B, S, H, 128]) must be given: the call allocates nothing.
+    """
+    lib = load_library()
+    dev = q.device
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, name, torch.bfloat16, dev, (B, S, H, D))
+    _need(vbs, "vbs", torch.int32, dev, (S // BLOCK,))
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    if topk_idx.dim() != 4 or tuple(topk_idx.shape[:3]) != (B, H, S // BLOCK):
+        raise ValueError(f"topk_idx has shape {tuple(topk_idx.shape)}, expected (B, H, S/64, topk)")
+    st = lib.vsa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S,
+                             H, D, topk_idx.shape[3], _default_scale(sm_scale), _stream(dev))
+    _check("vsa_fwd_noalloc", st)
     return out
 
 

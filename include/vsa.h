@@ -64,7 +64,8 @@ typedef enum vsa_status {
   VSA_ERR_UNSUPPORTED = 4, /* head_dim != 128                                     */
   VSA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch            */
   VSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
-  VSA_ERR_VALUE = 7        /* sm_scale negative, NaN or infinite                  */
+  VSA_ERR_VALUE = 7,       /* sm_scale negative, NaN or infinite                  */
+  VSA_ERR_SCRATCH = 8      /* vsa_fwd_noalloc: the shape exceeds its fixed scratch */
 } vsa_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -113,6 +114,27 @@ vsa_status vsa_fwd(const void* q, const void* k, const void* v,
                    int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
                    int32_t topk, float sm_scale,
                    void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+
+/*
+ * vsa_fwd_noalloc -- vsa_fwd for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, result and errors as vsa_fwd, minus the workspace: the
+ * packed V tiles go to a fixed scratch array of vsa_fwd_noalloc_max_bytes()
+ * bytes (64 MiB) that the library holds on each GPU it runs on until the
+ * process ends.  VSA_ERR_SCRATCH when the shape needs more than that, i.e.
+ * when batch * num_heads * seq_len/64 tiles of 16 KB (plus one byte each,
+ * 256-byte aligned) exceed it (about 4090 tiles: config 1's 8 x 84 fits, the
+ * 40 x 624 Wan2.2 shape does not).  The call allocates nothing and touches no
+ * memory allocator.  Every call on one GPU shares that GPU's array, which is
+ * fully rewritten by each call: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.
+ */
+size_t vsa_fwd_noalloc_max_bytes(void);
+vsa_status vsa_fwd_noalloc(const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, const int32_t* vbs, void* out,
+                           int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                           int32_t topk, float sm_scale, vsa_stream_t stream);
 
 /*
  * The two stages of vsa_fwd, for callers that time or schedule them apart.

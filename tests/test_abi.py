@@ -32,14 +32,15 @@ def test_every_declared_function_is_exported(lib):
             "vsa_fwd_prepacked",
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
             "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk",
-            "vsa_route_workspace_size", "vsa_kc_stats"} <= set(names)
+            "vsa_route_workspace_size", "vsa_kc_stats", "vsa_fwd_noalloc",
+            "vsa_fwd_noalloc_max_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert native.status_string(s).startswith("VSA_")
     assert native.status_string(99) == "VSA_ERR_UNKNOWN"
 
@@ -102,6 +103,19 @@ def test_stage_and_proxy_entry_points_reject_bad_arguments(lib):
     assert px(sel=15) == SHAPE
     assert px(scale=-2.0) == VALUE
     assert px(wsb=100) == WS
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_on_host(lib):
+    """vsa_fwd_noalloc checks the shape first, then its fixed scratch: the
+    Wan2.2 shape (40 x 624 tiles of 16 KB) exceeds the 64 MiB array."""
+    assert lib.vsa_fwd_noalloc_max_bytes() == 64 << 20
+    call = lambda **kw: lib.vsa_fwd_noalloc(  # noqa: E731
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, kw.get("S", 39936), kw.get("H", 40), 128,
+        kw.get("topk", 78), 0.088, None)
+    assert call() == 8                       # VSA_ERR_SCRATCH
+    assert call(topk=0) == SHAPE             # shape errors come first
+    assert lib.vsa_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, 2, 0.1,
+                               None) == NULL
 
 
 def test_kc_stats_rejects_bad_arguments_on_host(lib):
