@@ -420,6 +420,9 @@ def main():
                     help="tile: the cube tile/untile layout kernels on the config's grid; "
                          "merge: the merge of two partial results at the config's shape")
     ap.add_argument("--cpu-items", type=int, default=4000)
+    ap.add_argument("--protocol-rounds", type=int, default=5,
+                    help="after the timed steps: rounds of event-timed samples (0: skip)")
+    ap.add_argument("--protocol-samples", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run plain device copies of this many MiB "
@@ -511,6 +514,29 @@ def main():
     log(f"step {ms_per_step:.3f} ms (pack {pack_ms.mean():.3f} ms, attention avg {attn_avg:.3f} "
         f"p50 {np.median(attn_ms):.3f} min {attn_ms.min():.3f} ms), {value:.1f} TFLOP/s effective")
 
+    # The pages' timing protocol (PR page, Proxy overhead: five balanced rounds
+    # of 80 event-timed samples, p50 reported), after the timed steps above.
+    proto = None
+    if args.protocol_rounds > 0:
+        samples_attn, samples_step = [], []
+        for _ in range(args.protocol_rounds):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.protocol_samples)]
+            for e in ev:
+                step(e)
+            torch.cuda.synchronize()
+            samples_attn += [e[1].elapsed_time(e[2]) for e in ev]
+            samples_step += [e[0].elapsed_time(e[2]) for e in ev]
+        a, st_ = np.array(samples_attn), np.array(samples_step)
+        proto = {"rounds": args.protocol_rounds, "samples_per_round": args.protocol_samples,
+                 "attention_ms": {"p50": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+                                  "mean": round(float(a.mean()), 4)},
+                 "call_ms": {"p50": round(float(np.median(st_)), 4), "min": round(float(st_.min()), 4),
+                             "mean": round(float(st_.mean()), 4)},
+                 "attention_p50_tflops": round(f_eff / (float(np.median(a)) * 1e-3) / 1e12, 2)}
+        log(f"protocol {args.protocol_rounds} x {args.protocol_samples}: attention p50 "
+            f"{proto['attention_ms']['p50']:.3f} ms, call p50 {proto['call_ms']['p50']:.3f} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_items)
@@ -544,6 +570,7 @@ def main():
                      "traffic": measured_traffic(cfg.name),
                      "traffic_unit": "bytes per launch, HBM side (copy-calibrated FETCH_SIZE + WRITE_SIZE)"},
         "counters": measured_counters(cfg.name),
+        "timing_protocol": proto,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
