@@ -423,6 +423,8 @@ def main():
     ap.add_argument("--protocol-rounds", type=int, default=5,
                     help="after the timed steps: rounds of event-timed samples (0: skip)")
     ap.add_argument("--protocol-samples", type=int, default=80)
+    ap.add_argument("--shared-sweep-steps", type=int, default=20,
+                    help="also time this many steps with the timing-dependent tile order (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run plain device copies of this many MiB "
@@ -485,13 +487,13 @@ def main():
     scale = float(wl.sm_scale)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step(ev=None, shared_sweep=False):
         if ev is not None:
             ev[0].record(stream)
         vsa.vsa_pack_values(v, vbs, ws)
         if ev is not None:
             ev[1].record(stream)
-        vsa.vsa_fwd_prepacked(q, k, topk, vbs, ws, scale, out=out)
+        vsa.vsa_fwd_prepacked(q, k, topk, vbs, ws, scale, out=out, shared_sweep=shared_sweep)
         if ev is not None:
             ev[2].record(stream)
 
@@ -537,6 +539,26 @@ def main():
         log(f"protocol {args.protocol_rounds} x {args.protocol_samples}: attention p50 "
             f"{proto['attention_ms']['p50']:.3f} ms, call p50 {proto['call_ms']['p50']:.3f} ms")
 
+    # The same steps with the timing-dependent tile order (VSA_FLAG_SHARED_SWEEP),
+    # reported beside the default, reproducible order that gives `value`.
+    shared = None
+    if args.shared_sweep_steps > 0:
+        for _ in range(3):
+            step(shared_sweep=True)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.shared_sweep_steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for e in sev:
+            step(e, shared_sweep=True)
+        torch.cuda.synchronize()
+        sms = (time.perf_counter() - t1) * 1e3 / args.shared_sweep_steps
+        sattn = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+        shared = {"ms_per_step": round(sms, 4), "attention_avg_ms": round(sattn, 4),
+                  "value": round(f_eff / (sms * 1e-3) / 1e12, 2),
+                  "attention_frac_of_peak": round(f_eff / (sattn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"shared sweep: step {sms:.3f} ms, attention avg {sattn:.3f} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_items)
@@ -571,6 +593,7 @@ def main():
                      "traffic_unit": "bytes per launch, HBM side (copy-calibrated FETCH_SIZE + WRITE_SIZE)"},
         "counters": measured_counters(cfg.name),
         "timing_protocol": proto,
+        "shared_sweep_order": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

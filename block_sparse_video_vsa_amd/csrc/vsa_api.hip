@@ -88,7 +88,7 @@ extern "C" const char* vsa_status_string(vsa_status s) {
     case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED: head_dim must be 128";
     case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE: workspace missing or too small";
-    case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale must be finite and >= 0";
+    case VSA_ERR_VALUE: return "VSA_ERR_VALUE: sm_scale not finite and >= 0, or unknown flags";
     case VSA_ERR_SCRATCH:
       return "VSA_ERR_SCRATCH: the shape needs more scratch than the fixed buffer of vsa_fwd_noalloc";
   }
@@ -158,7 +158,7 @@ vsa_status enqueue_pack(const void* v, const int32_t* vbs, int32_t batch, int32_
 vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
                           const int32_t* vbs, void* out, int32_t batch, int32_t seq_len,
                           int32_t num_heads, int32_t topk, float sm_scale, void* workspace,
-                          hipStream_t s, float* lse = nullptr) {
+                          hipStream_t s, float* lse = nullptr, uint32_t flags = 0) {
   const int nblk = seq_len / kBlock;
   const WsLayout ws = ws_layout(batch, num_heads, nblk, 0);
   uint8_t* wsb = (uint8_t*)workspace;
@@ -174,6 +174,7 @@ vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
   p.seg_tiles = topk;
   p.table_cap = topk;
   p.lse = lse;
+  p.sweep_rate = (flags & VSA_FLAG_SHARED_SWEEP) ? 1.0f : 0.0f;   // set from the shape at launch
   return launch_attn(p, false, s) == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH;
 }
 
@@ -242,6 +243,36 @@ extern "C" vsa_status vsa_fwd_noalloc(const void* q, const void* k, const void* 
   st = enqueue_pack(v, vbs, batch, seq_len, num_heads, ws, s);
   if (st != VSA_OK) return st;
   return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale, ws, s);
+}
+
+extern "C" vsa_status vsa_fwd_ex(const void* q, const void* k, const void* v,
+                                 const int32_t* topk_idx, const int32_t* vbs, void* out,
+                                 int32_t batch, int32_t seq_len, int32_t num_heads,
+                                 int32_t head_dim, int32_t topk, float sm_scale, uint32_t flags,
+                                 void* workspace, size_t workspace_bytes, vsa_stream_t stream) {
+  if (flags & ~(uint32_t)VSA_FLAG_SHARED_SWEEP) return VSA_ERR_VALUE;
+  vsa_status st = check_fwd(q, k, v, topk_idx, vbs, out, batch, seq_len, num_heads, head_dim,
+                            topk, sm_scale, workspace, workspace_bytes, true, true);
+  if (st != VSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = enqueue_pack(v, vbs, batch, seq_len, num_heads, workspace, s);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
+                        workspace, s, nullptr, flags);
+}
+
+extern "C" vsa_status vsa_fwd_prepacked_ex(const void* q, const void* k, const int32_t* topk_idx,
+                                           const int32_t* vbs, void* out, int32_t batch,
+                                           int32_t seq_len, int32_t num_heads, int32_t head_dim,
+                                           int32_t topk, float sm_scale, uint32_t flags,
+                                           const void* workspace, size_t workspace_bytes,
+                                           vsa_stream_t stream) {
+  if (flags & ~(uint32_t)VSA_FLAG_SHARED_SWEEP) return VSA_ERR_VALUE;
+  vsa_status st = check_fwd(q, k, nullptr, topk_idx, vbs, out, batch, seq_len, num_heads,
+                            head_dim, topk, sm_scale, workspace, workspace_bytes, true, false);
+  if (st != VSA_OK) return st;
+  return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
+                        (void*)workspace, (hipStream_t)stream, nullptr, flags);
 }
 
 extern "C" vsa_status vsa_fwd_lse(const void* q, const void* k, const void* v,

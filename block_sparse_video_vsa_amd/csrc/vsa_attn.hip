@@ -33,13 +33,12 @@
 // Tile order (it changes results only by rounding): the exact fp16 tiles of an
 // item are swept in ascending block order from a start block, in nseg segments
 // of the block range; inside a segment they go kind by kind (full, full with
-// padding keys, half, half with padding keys), each kind through a straight-line
-// specialisation of the tile step, so the accumulators never cross
-// data-dependent control flow except the rescale.  Proxy and bf16 tiles follow.
-// The start block follows from the workgroup's dispatch slot so that the
-// resident workgroups of a head move through its blocks together and the XCD's
-// L2 holds a narrow window of that head's K/V tiles instead of all of them; it
-// depends on nothing but the shapes, so every call gives the same bits.
+// padding keys, half, half with padding keys, quarter), each kind through a
+// straight-line specialisation of the tile step, so the accumulators never
+// cross data-dependent control flow except the rescale.  Proxy and bf16 tiles
+// follow.  The start block comes from the workgroup's dispatch slot (the
+// default: every call gives the same bits) or, on request, from the real-time
+// counter (a shared sweep with better L2 reuse; see the kernel prologue).
 #include "vsa_internal.h"
 
 #include <math.h>
@@ -715,12 +714,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int ncell = kKinds * nseg + 2;
   int* ccnt = sCell;                     // [ncell] tiles per cell
   int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
-  // Start block of the sweep, from the dispatch slot: workgroup i of an XCD
-  // starts about when workgroup i - 128 ends (128 are resident per XCD), and
-  // each finished sweep advances the average position of the resident ones by
-  // nblk / 128 blocks, so slot i joins them at i * nblk / 128.  The order
-  // depends on the shapes only, so results are reproducible bit for bit.
-  const int start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
+  // Start block of the sweep.  Reproducible order: from the dispatch slot, so
+  // that the 128 workgroups resident on an XCD at once start spread evenly
+  // over the head's blocks (a slot's later items start where its first did),
+  // and the order depends on the shapes only.  Shared sweep (sweep_rate > 0):
+  // from the real-time counter, at sweep_rate blocks per tick, about the rate
+  // at which a workgroup moves through its blocks; the resident workgroups of
+  // a head then move through its blocks together, a narrow window of its K/V
+  // tiles stays in the XCD's L2, and the order depends on timing.
+  int start;
+  if (p.sweep_rate > 0.0f) {
+    const double pos = (double)__builtin_amdgcn_s_memrealtime() * (double)p.sweep_rate;
+    start = (int)fmod(pos, (double)p.nblk);
+  } else {
+    start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
+  }
   for (int t = tid; t < 2 * ncell + 1; t += kThreads) sCell[t] = 0;
   wg_barrier();
   for (int t = tid; t < ncand; t += kThreads) {
@@ -907,6 +915,13 @@ size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
 hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream) {
   if (params.n_items <= 0) return hipSuccess;
   AttnParams p = params;
+  // Shared sweep: a workgroup crosses about one tile per kTicksPerTile ticks of
+  // the 100 MHz real-time counter (MI355X, configs 2 and 3b: 2.0-2.2 us per
+  // 64-key tile per workgroup), so its blocks pass at nblk / (tiles *
+  // kTicksPerTile) per tick.
+  constexpr float kTicksPerTile = 200.0f;
+  if (p.sweep_rate > 0.0f)
+    p.sweep_rate = (float)p.nblk / ((float)std::max(1, p.seg_tiles) * kTicksPerTile);
   const size_t dyn = attn_dyn_lds(p, proxy);
   // about ten tiles of a typical item per sweep segment
   const int tiles = p.seg_tiles;

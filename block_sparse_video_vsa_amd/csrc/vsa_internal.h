@@ -104,6 +104,7 @@ struct AttnParams {
   int table_cap;            // tile-table capacity (entries)
   int nseg;                 // sweep segments per item (1..kMaxSeg)
   int seg_tiles;            // tiles of a typical item (sizes the segments)
+  float sweep_rate;         // > 0: shared sweep, start block from the real-time counter
   float c;                  // sm_scale * log2(e)
   // proxy prefix split (appended: the fields above keep their offsets)
   int items_per_bh;         // nblk, or (proxy) nprefix * psplit + nvideo

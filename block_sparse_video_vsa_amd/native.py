@@ -35,6 +35,12 @@ _SIGNATURES = {
     "vsa_fwd_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "vsa_fwd": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p, _size_t, _c_void_p]),
+    "vsa_fwd_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_uint32, _c_void_p,
+                                  _size_t, _c_void_p]),
+    "vsa_fwd_prepacked_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_uint32,
+                                            _c_void_p, _size_t, _c_void_p]),
     "vsa_fwd_noalloc_max_bytes": (_size_t, []),
     "vsa_fwd_noalloc": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _c_void_p]),
@@ -76,6 +82,7 @@ _SIGNATURES = {
 }
 
 VSA_OK = 0
+FLAG_SHARED_SWEEP = 1      # VSA_FLAG_SHARED_SWEEP
 
 
 class VSAError(RuntimeError):
@@ -170,10 +177,11 @@ def proxy_workspace_size(batch: int, seq_len: int, prefix_len: int, heads: int,
                                                            head_dim))
 
 
-def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale=None, out=None, workspace=None):
+def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale=None, out=None, workspace=None, shared_sweep=False):
     """Fine block-sparse attention forward (C ABI vsa_fwd) on q's device and current stream.
 
     q, k, v: bf16 [B, S, H, 128]; topk_idx: int32 [B, H, S/64, topk]; vbs: int32 [S/64].
+    shared_sweep: the timing-dependent tile order (vsa_fwd_ex, VSA_FLAG_SHARED_SWEEP).
     Returns out (bf16 [B, S, H, 128]).
     """
     lib = load_library()
@@ -191,6 +199,12 @@ def vsa_fwd(q, k, v, topk_idx, vbs, sm_scale=None, out=None, workspace=None):
     nbytes = fwd_workspace_size(B, S, H, D)
     if workspace is None:
         workspace = _workspace(dev, max(nbytes, 1))
+    if shared_sweep:
+        st = lib.vsa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S, H,
+                            D, topk_idx.shape[3], _default_scale(sm_scale), FLAG_SHARED_SWEEP,
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+        _check("vsa_fwd_ex", st)
+        return out
     st = lib.vsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S, H, D,
                      topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
                      workspace.numel(), _stream(dev))
@@ -230,8 +244,9 @@ def vsa_pack_values(v, vbs, workspace):
     _check("vsa_pack_values", st)
 
 
-def vsa_fwd_prepacked(q, k, topk_idx, vbs, workspace, sm_scale=None, out=None):
-    """Second stage of vsa_fwd: attention over a workspace filled by vsa_pack_values."""
+def vsa_fwd_prepacked(q, k, topk_idx, vbs, workspace, sm_scale=None, out=None, shared_sweep=False):
+    """Second stage of vsa_fwd: attention over a workspace filled by vsa_pack_values
+    (vsa_fwd_prepacked_ex with VSA_FLAG_SHARED_SWEEP when shared_sweep)."""
     lib = load_library()
     dev = q.device
     B, S, H, D = q.shape
@@ -241,6 +256,13 @@ def vsa_fwd_prepacked(q, k, topk_idx, vbs, workspace, sm_scale=None, out=None):
     _need(topk_idx, "topk_idx", torch.int32, dev)
     if out is None:
         out = torch.empty_like(q)
+    if shared_sweep:
+        st = lib.vsa_fwd_prepacked_ex(_ptr(q), _ptr(k), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S,
+                                      H, D, topk_idx.shape[3], _default_scale(sm_scale),
+                                      FLAG_SHARED_SWEEP, _ptr(workspace), workspace.numel(),
+                                      _stream(dev))
+        _check("vsa_fwd_prepacked_ex", st)
+        return out
     st = lib.vsa_fwd_prepacked(_ptr(q), _ptr(k), _ptr(topk_idx), _ptr(vbs), _ptr(out), B, S, H,
                                D, topk_idx.shape[3], _default_scale(sm_scale), _ptr(workspace),
                                workspace.numel(), _stream(dev))

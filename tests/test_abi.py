@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported(lib):
             "vsa_cube_count", "vsa_cube_vbs", "vsa_tile", "vsa_untile", "vsa_fwd_lse",
             "vsa_merge", "vsa_fwd_proxy_bitmask", "vsa_fwd_proxy_bsr", "vsa_route_topk",
             "vsa_route_workspace_size", "vsa_kc_stats", "vsa_fwd_noalloc",
-            "vsa_fwd_noalloc_max_bytes"} <= set(names)
+            "vsa_fwd_noalloc_max_bytes", "vsa_fwd_ex", "vsa_fwd_prepacked_ex"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(native._SIGNATURES) == set(names)
@@ -116,6 +116,16 @@ def test_noalloc_rejects_shapes_beyond_its_scratch_on_host(lib):
     assert call(topk=0) == SHAPE             # shape errors come first
     assert lib.vsa_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, 2, 0.1,
                                None) == NULL
+
+
+def test_fwd_ex_rejects_unknown_flags_on_host(lib):
+    ex = lambda flags, topk=2: lib.vsa_fwd_ex(  # noqa: E731
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, topk, 0.088, flags, FAKE, 1 << 30, None)
+    assert ex(2) == VALUE
+    assert ex(1 << 31) == VALUE
+    assert ex(1, topk=0) == SHAPE
+    assert lib.vsa_fwd_prepacked_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 512, 2, 128, 2, 0.088, 4, FAKE,
+                                    1 << 30, None) == VALUE
 
 
 def test_kc_stats_rejects_bad_arguments_on_host(lib):

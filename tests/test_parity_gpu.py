@@ -113,6 +113,38 @@ def test_large_configs_every_row(dev, name, heads):
     assert g.ok(), str(g)
 
 
+def test_config2_shared_sweep_every_row(dev):
+    """The timing-dependent tile order (VSA_FLAG_SHARED_SWEEP) on the full
+    config-2 output, every valid row graded; it differs from the default order
+    only by rounding."""
+    wl = workload("2")
+    out = from_dev(vsa.vsa_fwd(to_dev(wl.q, dev, True), to_dev(wl.k, dev, True),
+                               to_dev(wl.v, dev, True), to_dev(wl.topk_idx, dev),
+                               to_dev(wl.vbs, dev), float(wl.sm_scale), shared_sweep=True))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(O.bf16_to_f64(out))), "non-finite output"
+    assert pad_rows_zero(out, wl.vbs)
+    g = grade_every_item(out, wl.vbs, lambda b, h, c: O.vsa_fwd_item(
+        wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale, b, h, c))
+    print(f"config 2, shared sweep, every valid row: {g}")
+    assert g.ok(), str(g)
+    d = np.abs(O.bf16_to_f64(out) - O.bf16_to_f64(fwd_output(dev, "2")))
+    assert d.max() <= 2.0 ** -6 * max(1.0, float(np.abs(O.bf16_to_f64(out)).max()))
+
+
+def test_small_configs_shared_sweep(dev):
+    for name in ("0", "1"):
+        wl = W.generate(name)
+        out = from_dev(vsa.vsa_fwd(to_dev(wl.q, dev, True), to_dev(wl.k, dev, True),
+                                   to_dev(wl.v, dev, True), to_dev(wl.topk_idx, dev),
+                                   to_dev(wl.vbs, dev), float(wl.sm_scale), shared_sweep=True))
+        torch.cuda.synchronize()
+        o64 = O.vsa_fwd(wl.q, wl.k, wl.v, wl.topk_idx, wl.vbs, wl.sm_scale)
+        g = grade_full(out, o64, wl.vbs)
+        assert pad_rows_zero(out, wl.vbs)
+        assert g.ok(), f"config {name}: {g}"
+
+
 def test_config2_repeats_bitwise(dev):
     """The tile order depends on the shapes only: a repeated call on the
     full-size workload is bitwise identical."""
