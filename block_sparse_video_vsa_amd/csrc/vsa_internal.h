@@ -124,7 +124,6 @@ hipError_t launch_attn(const AttnParams& p, bool proxy, hipStream_t stream);
 hipError_t launch_kc_stats(const uint16_t* kc, const int32_t* vbs, float* mean, float* var,
                            int batch, int nblk, int heads, int first, int count,
                            hipStream_t stream);
-// Routing: top-k key blocks by block-mean scores.
 // Routing: top-k key blocks by block-mean scores, through an fp64 score
 // workspace that holds route_pairs_per_chunk (batch, head) pairs at a time.
 int route_pairs_per_chunk(int batch, int heads, int nblk);
