@@ -10,7 +10,10 @@
 // whose probability counts vbs times in the softmax denominator.
 //
 // Work decomposition: one workgroup of two wave64s per (batch, head, query
-// block); wave w owns query rows 32w..32w+31.  For each selected KV tile:
+// block); wave w owns query rows 32w..32w+31.  A block with at most 32 valid
+// query rows gives both waves rows 0..31 instead, each wave taking one 32-key
+// half of every tile with its own running softmax, and the two partial results
+// are merged at the end.  For each selected KV tile:
 //
 //   S^T (64 keys x 32 queries) = K . Q^T   bf16 MFMA 32x32x16, fp32 accumulate
 //   online softmax in exp2, fp32, one query per lane column
@@ -27,8 +30,8 @@
 // its sixteen 16-byte chunks XOR-swizzled by the row index, so the MFMA A-operand
 // reads (32 rows, one chunk each) spread over all LDS banks.  V tiles are read
 // from the packed key-major copy written by pack_vt_kernel, which already has
-// the LDS layout, so their copy is linear.  Tiles whose vbs is <= 32 load and
-// multiply only their first 32 keys.
+// the LDS layout, so their copy is linear.  Tiles whose vbs is <= 32 (<= 16)
+// load and multiply only their first 32 (16) keys.
 //
 // Tile order (it changes results only by rounding): the exact fp16 tiles of an
 // item are swept in ascending block order from a start block, in nseg segments
@@ -277,10 +280,11 @@ __device__ inline float proxy_weight(const uint8_t* wts, int kb, int i, int hh) 
 // units), and a rescale of O and the row sum when it exceeds the running max
 // by more than kRescaleSlack.
 // NI registers of each 32-key half take part: 16, or 8 (keys 0-15) for
-// quarter tiles, whose keys 16-31 are not loaded.
+// quarter tiles, whose keys 16-31 are not loaded.  s[kb] holds key half
+// kb0 + kb.
 template <int NKB, int NI, int MODE>
 __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts, float c, int hh,
-                                State& st) {
+                                State& st, int kb0) {
   float t = -INFINITY;
   if (MODE == kModeProxy) {
     // a proxy logit is offset by log2 of its weight (-inf for weight 0)
@@ -288,13 +292,13 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        t = fmaxf(t, fmaf(s[kb][i], c, __log2f(proxy_weight(wts, kb, i, hh))));
+        t = fmaxf(t, fmaf(s[kb][i], c, __log2f(proxy_weight(wts, kb0 + kb, i, hh))));
     t = pair_max(t);
   } else if (MODE == kModePad) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) t = fmaxf(t, key_of(kb, i, hh) < nv ? s[kb][i] : -INFINITY);
+      for (int i = 0; i < NI; ++i) t = fmaxf(t, key_of(kb0 + kb, i, hh) < nv ? s[kb][i] : -INFINITY);
     t = pair_max(t) * c;
   } else {
 #pragma unroll
@@ -471,18 +475,25 @@ __device__ inline void issue_tile_v(const Ctx& x, int e) {
 // tile's K rows, running max, wait for its V, probabilities and O += P V,
 // release V and prefetch the next tile's V.  NKB / MODE / BF16 are fixed per
 // tile kind (MODE kModeAny: bf16 tiles, exact or proxy, decided per tile).
-template <bool kProxy, bool kCompute, int TS, int MODE, bool BF16>
+// Key split (kKS, items with at most 32 valid query rows): both waves hold
+// the same 32 query rows; wave w takes key half w of a full tile, and a half
+// or quarter tile (all keys in half 0) goes to the wave for which `mine` is
+// set.  Each wave then keeps its own running max, row sum and O, merged at
+// the end of the item.  Copies and barriers are the same in both modes.
+template <bool kProxy, int TS, int MODE, bool BF16, bool kKS>
 __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st, int e, int en,
-                                 bool has_next) {
-  constexpr int NKB = TS == kTsFull ? 2 : 1;       // 32-key halves of S
+                                 bool has_next, bool mine) {
+  constexpr int NKB = (TS == kTsFull && !kKS) ? 2 : 1;   // 32-key halves of S
   constexpr int NI = TS == kTsQuarter ? 8 : 16;    // registers per half that hold loaded keys
   constexpr int NK2 = TS == kTsQuarter ? 1 : 2;    // 16-key steps of O += P V per half
+  const int kb0 = (kKS && TS == kTsFull) ? x.w : 0;   // first key half this wave takes
+  const bool work = !kKS || TS == kTsFull || mine;
   // K(j) has landed once only V(j)'s copies (8, 4 or 2 instructions per wave)
   // are still in flight.
   wait_vmcnt<(8 >> TS)>();
   wg_barrier();
   f32x16 s[2];
-  if (kCompute) s_tile<NKB>(x.sk, qop, x.ln, x.hh, s);
+  if (work) s_tile<NKB>(x.sk + kb0 * 8192, qop, x.ln, x.hh, s);
   wg_barrier();   // both waves are done with sK
   if (has_next) issue_tile_k<kProxy>(x, en);
 
@@ -492,12 +503,12 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   // The running max, the probabilities and O += P V run at raised wave
   // priority: where both waves of a SIMD can issue, this phase goes first.
   __builtin_amdgcn_s_setprio(2);
-  if (kCompute) {
+  if (work) {
     if (MODE == kModeAny) {
-      if (px) tile_max<NKB, NI, kModeProxy>(s, nv, wts, x.c, x.hh, st);
-      else tile_max<NKB, NI, kModePad>(s, nv, wts, x.c, x.hh, st);
+      if (px) tile_max<NKB, NI, kModeProxy>(s, nv, wts, x.c, x.hh, st, kb0);
+      else tile_max<NKB, NI, kModePad>(s, nv, wts, x.c, x.hh, st, kb0);
     } else {
-      tile_max<NKB, NI, MODE>(s, nv, wts, x.c, x.hh, st);
+      tile_max<NKB, NI, MODE>(s, nv, wts, x.c, x.hh, st, kb0);
     }
   }
 
@@ -512,18 +523,19 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
     wait_vmcnt<0>();
   }
   wg_barrier();
-  if (kCompute) {
+  if (work) {
     const float nmc = -st.mc;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      const int kh = kb0 + kb;
       unsigned pk[8], pl[8];
       if (MODE == kModeAny) {
-        if (px) half_probs<kModeProxy, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
-        else half_probs<kModePad, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        if (px) half_probs<kModeProxy, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        else half_probs<kModePad, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       } else {
-        half_probs<MODE, BF16, kProxy, NI>(s[kb], kb, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        half_probs<MODE, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       }
-      pv_half<BF16, kProxy, NK2>(x.sv, kb, pk, pl, x.ln, x.hh, st);
+      pv_half<BF16, kProxy, NK2>(x.sv, kh, pk, pl, x.ln, x.hh, st);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -537,7 +549,7 @@ __device__ inline int cell_bf16(int nseg) { return kKinds * nseg + 1; }
 
 // All tiles of one item in the order of `ord`; cbeg[c] is the first position of
 // cell c (cbeg[kKinds nseg + 2] = number of tiles).
-template <bool kProxy, bool kCompute>
+template <bool kProxy, bool kKS>
 __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st, const int* ord,
                                  const int* cbeg, int nseg, int n) {
   const int e0 = __builtin_amdgcn_readfirstlane(ord[0]);
@@ -550,20 +562,20 @@ __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st
       const int e = __builtin_amdgcn_readfirstlane(ord[j]);
       const bool has_next = j + 1 < n;
       const int en = has_next ? __builtin_amdgcn_readfirstlane(ord[j + 1]) : 0;
-      body(e, en, has_next);
+      body(e, en, has_next, (j & 1) == x.w);   // key split: half tiles alternate between the waves
     }
   };
   for (int s = 0; s < nseg; ++s) {
     const int c0 = kKinds * s;
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeFull, false>(x, qop, st, e, en, hn); }, c0 + kGFull);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGFullPad);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsHalf, kModeFull, false>(x, qop, st, e, en, hn); }, c0 + kGHalf);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsHalf, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGHalfPad);
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsQuarter, kModePad, false>(x, qop, st, e, en, hn); }, c0 + kGQuarter);
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsFull, kModeFull, false, kKS>(x, qop, st, e, en, hn, mi); }, c0 + kGFull);
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsFull, kModePad, false, kKS>(x, qop, st, e, en, hn, mi); }, c0 + kGFullPad);
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsHalf, kModeFull, false, kKS>(x, qop, st, e, en, hn, mi); }, c0 + kGHalf);
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsHalf, kModePad, false, kKS>(x, qop, st, e, en, hn, mi); }, c0 + kGHalfPad);
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsQuarter, kModePad, false, kKS>(x, qop, st, e, en, hn, mi); }, c0 + kGQuarter);
   }
   if (kProxy)
-    cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeProxy, false>(x, qop, st, e, en, hn); }, cell_proxy(nseg));
-  cell([&](int e, int en, bool hn) { tile_step<kProxy, kCompute, kTsFull, kModeAny, true>(x, qop, st, e, en, hn); }, cell_bf16(nseg));
+    cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsFull, kModeProxy, false, kKS>(x, qop, st, e, en, hn, mi); }, cell_proxy(nseg));
+  cell([&](int e, int en, bool hn, bool mi) { tile_step<kProxy, kTsFull, kModeAny, true, kKS>(x, qop, st, e, en, hn, mi); }, cell_bf16(nseg));
 }
 
 template <bool kProxy>
@@ -796,8 +808,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---------------- per-wave state ---------------------------------------
   const int n = __builtin_amdgcn_readfirstlane(cbeg[ncell]);
-  const bool active = 32 * w < vq;      // wave has at least one valid query row
-  const int qrow = 32 * w + ln;         // query row inside the block
+  // Blocks with at most 32 valid query rows split the keys of each tile
+  // between the two waves instead of leaving the second wave without rows.
+  const bool ks = vq <= 32;
+  int qrow = ks ? ln : 32 * w + ln;     // query row inside the block
   bf16x8 qop[8];
   {
     const uint16_t* qp = p.q + (((int64_t)b * p.seq + (int64_t)qb * kBlock + qrow) * p.heads + h) *
@@ -840,13 +854,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   st.mc = -INFINITY;
   st.lsum = 0.0f;
   if (n > 0) {
-    if (active) run_tiles<kProxy, true>(x, qop, st, ord, cbeg, nseg, n);
+    if (ks) run_tiles<kProxy, true>(x, qop, st, ord, cbeg, nseg, n);
     else run_tiles<kProxy, false>(x, qop, st, ord, cbeg, nseg, n);
+  }
+  bool active = true;                   // this wave writes the rows it computed
+  if (ks) {
+    // Merge the two waves' partial results over disjoint keys: wave 1 hands
+    // its O, running max and row sum to wave 0 through the tile buffers (no
+    // copy is in flight after the last tile, and both waves have passed its
+    // final barrier), and then writes the padding rows 32..63.
+    float* so = (float*)sK;             // 64 accumulator registers x 64 lanes = 16 KB
+    float* sm = (float*)sV;
+    if (w == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        so[(0 * 16 + r) * 64 + lane] = st.o0[r];
+        so[(1 * 16 + r) * 64 + lane] = st.o1[r];
+        so[(2 * 16 + r) * 64 + lane] = st.o2[r];
+        so[(3 * 16 + r) * 64 + lane] = st.o3[r];
+      }
+      sm[lane] = st.mc;
+      sm[64 + lane] = st.lsum;
+    }
+    wg_barrier();
+    if (w == 0) {
+      const float m1 = sm[lane], l1 = sm[64 + lane];
+      const float m = fmaxf(st.mc, m1);
+      const float a0 = st.mc == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.mc - m);
+      const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.o0[r] = st.o0[r] * a0 + so[(0 * 16 + r) * 64 + lane] * a1;
+        st.o1[r] = st.o1[r] * a0 + so[(1 * 16 + r) * 64 + lane] * a1;
+        st.o2[r] = st.o2[r] * a0 + so[(2 * 16 + r) * 64 + lane] * a1;
+        st.o3[r] = st.o3[r] * a0 + so[(3 * 16 + r) * 64 + lane] * a1;
+      }
+      st.lsum = st.lsum * a0 + l1 * a1;
+      st.mc = m;
+    } else {
+      qrow = 32 + ln;
+      active = false;
+    }
   }
 
   // ---------------- epilogue ---------------------------------------------
   // o = O / l for valid rows; padding rows, empty rows and non-finite results
-  // are written as 0.  Lane (ln, hh) holds query row 32w+ln and, in register
+  // are written as 0.  Lane (ln, hh) holds query row qrow and, in register
   // 4a+r of accumulator db, head-dim index 32db + 8a + 4hh + r.
   const float l_tot = pair_sum(st.lsum);
   const bool row_ok = active && qrow < vq && l_tot > 0.0f;
