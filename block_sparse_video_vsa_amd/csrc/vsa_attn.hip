@@ -189,6 +189,10 @@ __device__ inline void split_bf16(float p0, float p1, unsigned& hi, unsigned& lo
 // klane ^ (((r0 + 4i) % 16) << 4) with klane = (l/16) * row_bytes +
 // (((l%16) ^ (l/16)) << 4).  Rows past rmax (proxy tiles beyond the last video
 // block) re-read row rmax.
+// Full and half tiles issue their copies in groups of four that share one
+// base address and one M0: the instruction's immediate offset (0, 1, 2, 3 KB)
+// moves the global address and the LDS destination alike, and each copy's
+// lane offset takes its 4j rows and subtracts the immediate again.
 template <int N, bool kMayClamp>
 __device__ inline void issue_k(const uint16_t* kbase, uint32_t row_bytes, int rmax, int r0,
                                uint32_t klane, int lane, unsigned char* sk) {
@@ -203,10 +207,29 @@ __device__ inline void issue_k(const uint16_t* kbase, uint32_t row_bytes, int rm
     const uint32_t rs = opaque_s(row_bytes);
     const char* kr = kb + (size_t)r0 * rs;
     const uint32_t m0 = opaque_s(l0 + (uint32_t)r0 * 256u);
+    if (N >= 4) {
+      // r0 is a multiple of 16 here, so copy j of each group uses chunk
+      // swizzle 4j (the lane offsets are the same for every tile).
+      uint32_t vo[4];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      dma16(kr, kl ^ (uint32_t)(((r0 + 4 * i) & 15) << 4), m0 + 1024u * i);
-      kr += 4 * rs;
+      for (int j = 0; j < 4; ++j) vo[j] = (klane ^ (uint32_t)((4 * j) << 4)) + 4u * j * rs - 1024u * j;
+#pragma unroll
+      for (int g = 0; g < N; g += 4)
+        asm volatile("s_mov_b32 m0, %5\n\t"
+                     "global_load_lds_dwordx4 %0, %4\n\t"
+                     "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+                     "global_load_lds_dwordx4 %3, %4 offset:3072"
+                     :
+                     : "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(kr + (size_t)g * 4 * rs),
+                       "s"(m0 + 1024u * g)
+                     : "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        dma16(kr, kl ^ (uint32_t)(((r0 + 4 * i) & 15) << 4), m0 + 1024u * i);
+        kr += 4 * rs;
+      }
     }
   } else {
     const int pcx = (lane & 15) ^ (lane >> 4);
@@ -221,15 +244,35 @@ __device__ inline void issue_k(const uint16_t* kbase, uint32_t row_bytes, int rm
 }
 
 // Issue the linear copy of N KB of one packed V tile starting at byte base;
-// vlane = 16 * lane.
+// vlane = 16 * lane.  Copies go in groups of up to four per base address and
+// M0, 1 KB apart through the immediate offset, which moves the global address
+// and the LDS destination alike.
 template <int N>
 __device__ inline void issue_v(const uint8_t* vtile, int base, uint32_t vlane, unsigned char* sv) {
+  static_assert(N == 2 || N % 4 == 0, "copies per wave: 2, 4 or 8");
   const uint32_t ob = opaque_s((uint32_t)base);   // not hoisted, as in issue_k
   const uint32_t m0 = opaque_s(lds_addr(sv) + ob);
   const uint8_t* vb = vtile + ob;
   const uint32_t vl = opaque_v(vlane);
+  if (N >= 4) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) dma16(vb + 1024 * i, vl, m0 + 1024u * i);
+    for (int g = 0; g < N; g += 4)
+      asm volatile("s_mov_b32 m0, %2\n\t"
+                   "global_load_lds_dwordx4 %0, %1\n\t"
+                   "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                   "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                   "global_load_lds_dwordx4 %0, %1 offset:3072"
+                   :
+                   : "v"(vl), "s"(vb + 1024 * g), "s"(m0 + 1024u * g)
+                   : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024"
+                 :
+                 : "v"(vl), "s"(vb), "s"(m0)
+                 : "memory");
+  }
 }
 
 // S^T (NKB x 32 keys, 32 queries) = K . Q^T.  Register i of s[kb] in lane
