@@ -71,21 +71,24 @@ constexpr float kRescaleSlack = 8.0f;
 
 
 // Tile-table entry: block/tile id (bits 0-19), valid rows (20-26), bf16 V (27),
-// proxy tile (28).
+// proxy tile (28), tile size (29-30, below).
 constexpr int kEntNvShift = 20;
 constexpr int kEntBf16 = 1 << 27;
 constexpr int kEntProxy = 1 << 28;
+constexpr int kEntSizeShift = 29;
 __device__ inline int ent_id(int e) { return e & 0xFFFFF; }
 __device__ inline int ent_nv(int e) { return (e >> kEntNvShift) & 127; }
 // Tile sizes: exact fp16 tiles load and multiply only the key rows their vbs
 // needs, in granules of 16: 64 (full), 32 (half) or 16 (quarter) keys.  bf16
-// and proxy tiles are always full.
+// and proxy tiles are always full.  The size is stored in the entry, so the
+// tile loop reads it with one bit-field extract.
 enum : int { kTsFull = 0, kTsHalf = 1, kTsQuarter = 2 };
-__device__ inline int ent_size(int e) {
-  if (e & (kEntBf16 | kEntProxy)) return kTsFull;
-  const int nv = ent_nv(e);
-  return nv > 32 ? kTsFull : nv > 16 ? kTsHalf : kTsQuarter;
+__device__ inline int make_ent(int id, int nv, bool bf16, bool proxy) {
+  const int ts = (bf16 || proxy || nv > 32) ? kTsFull : nv > 16 ? kTsHalf : kTsQuarter;
+  return id | (nv << kEntNvShift) | (bf16 ? kEntBf16 : 0) | (proxy ? kEntProxy : 0) |
+         (ts << kEntSizeShift);
 }
+__device__ inline int ent_size(int e) { return (e >> kEntSizeShift) & 3; }
 
 // Tile kinds, processed in this order within a sweep segment (the first
 // kKinds), then proxy and bf16 tiles.
@@ -475,6 +478,8 @@ struct Ctx {
   const uint8_t* wt;       // proxy denominator weights (valid rows, 0 = no key), per video block
   int b, h;
   int64_t bh_tiles;        // (b * heads + h) * nblk
+  const char* k_bh;        // K row 0 of this (batch, head)
+  const uint8_t* vt_bh;    // first packed V tile of this (batch, head)
   int64_t bh_proxy;        // (b * heads + h) * nproxy
   uint32_t row_bytes, klane, vlane;
   int w, lane, ln, hh, tid;
@@ -492,7 +497,7 @@ __device__ inline void issue_tile_k(const Ctx& x, int e) {
     base = p.kmean + (((int64_t)x.b * p.nblk + p.nprefix + (int64_t)kBlock * t) * p.heads + x.h) *
                          kHeadDim;
   } else {
-    base = p.k + (((int64_t)x.b * p.seq + (int64_t)ent_id(e) * kBlock) * p.heads + x.h) * kHeadDim;
+    base = (const uint16_t*)(x.k_bh + (uint64_t)(uint32_t)(ent_id(e) * kBlock) * x.row_bytes);
   }
   switch (ent_size(e)) {
     case kTsFull: issue_k<8, kProxy>(base, x.row_bytes, rmax, 32 * x.w, x.klane, x.lane, x.sk); break;
@@ -506,7 +511,7 @@ __device__ inline void issue_tile_v(const Ctx& x, int e) {
   const AttnParams& p = *x.p;
   const uint8_t* base = (kProxy && (e & kEntProxy))
                             ? p.pt + (x.bh_proxy + ent_id(e)) * kTileBytes
-                            : p.vt + (x.bh_tiles + ent_id(e)) * kTileBytes;
+                            : x.vt_bh + (uint64_t)(uint32_t)ent_id(e) * kTileBytes;
   switch (ent_size(e)) {
     case kTsFull: issue_v<8>(base, 8192 * x.w, x.vlane, x.sv); break;
     case kTsHalf: issue_v<4>(base, 4096 * x.w, x.vlane, x.sv); break;
@@ -758,12 +763,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     } else {
       const int pt = t - p.nprefix - width;
       const int rows = min(p.nvideo - kBlock * pt, kBlock);
-      return pt | (rows << kEntNvShift) | kEntProxy |
-             (p.pt_flags[(int64_t)bh * p.nproxy + pt] ? kEntBf16 : 0);
+      return make_ent(pt, rows, p.pt_flags[(int64_t)bh * p.nproxy + pt] != 0, true);
     }
     const int nv = (blk >= 0 && blk < p.nblk) ? min(max(p.vbs[blk], 0), kBlock) : 0;
     if (nv == 0) return -1;
-    return blk | (nv << kEntNvShift) | (p.vt_flags[bh_tiles + blk] ? kEntBf16 : 0);
+    return make_ent(blk, nv, p.vt_flags[bh_tiles + blk] != 0, false);
   };
   const int nseg = p.nseg;
   const int ncell = kKinds * nseg + 2;
@@ -879,6 +883,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   x.b = b;
   x.h = h;
   x.bh_tiles = bh_tiles;
+  x.k_bh = (const char*)(p.k + ((int64_t)b * p.seq * p.heads + h) * kHeadDim);
+  x.vt_bh = p.vt + bh_tiles * kTileBytes;
   x.bh_proxy = (int64_t)bh * p.nproxy;
   x.row_bytes = (uint32_t)(row_stride * 2);
   x.klane = (uint32_t)(lane >> 4) * x.row_bytes + (uint32_t)((((lane & 15) ^ (lane >> 4))) << 4);
