@@ -585,6 +585,17 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
       }
       pv_half<BF16, kProxy, NK2>(x.sv, kh, pk, pl, x.ln, x.hh, st);
     }
+    if (!BF16 && !kProxy) {
+      // V operand reads run four MFMAs ahead, across both key halves
+      constexpr int kR = 4 * NK2 * NKB;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < kR - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    }
   }
   __builtin_amdgcn_s_setprio(0);
   wg_barrier();   // both waves are done with sV
