@@ -614,14 +614,19 @@ __device__ inline void run_tiles(const Ctx& x, const bf16x8 (&qop)[8], State& st
   const int e0 = __builtin_amdgcn_readfirstlane(ord[0]);
   issue_tile_k<kProxy>(x, e0);
   issue_tile_v<kProxy>(x, e0);
+  // The entry of tile j + 1 is read from LDS one tile ahead (into a vector
+  // register), so that its read latency is not paid at the top of tile j.
+  int e_cur = e0;
+  int e_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(ord[1]) : 0;
   auto cell = [&](auto body, int c) {
     const int beg = __builtin_amdgcn_readfirstlane(cbeg[c]);
     const int end = __builtin_amdgcn_readfirstlane(cbeg[c + 1]);
     for (int j = beg; j < end; ++j) {
-      const int e = __builtin_amdgcn_readfirstlane(ord[j]);
       const bool has_next = j + 1 < n;
-      const int en = has_next ? __builtin_amdgcn_readfirstlane(ord[j + 1]) : 0;
-      body(e, en, has_next, (j & 1) == x.w);   // key split: half tiles alternate between the waves
+      const int v_after = j + 2 < n ? ord[j + 2] : 0;
+      body(e_cur, e_nxt, has_next, (j & 1) == x.w);   // key split: half tiles alternate between the waves
+      e_cur = e_nxt;
+      e_nxt = __builtin_amdgcn_readfirstlane(v_after);
     }
   };
   for (int s = 0; s < nseg; ++s) {
