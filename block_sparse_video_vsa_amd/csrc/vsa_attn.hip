@@ -374,9 +374,10 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
 // fp16 tiles fill pk with fp16 probabilities and, with kSplitP, pl with their
 // fp16 low parts (hi + lo, see f16_low_part); bf16 tiles always fill pk with the
 // high and pl with the low bf16 parts.  The plain forward keeps single fp16
-// probabilities (relative 2^-12 each); the proxy forward splits them, because
-// its value totals and long prefix rows leave less margin to the bf16 rounding
-// of the outputs, at the cost of twice the O += P V products.
+// probabilities (relative 2^-12 each); the proxy forward splits those of its
+// exact tiles, because its value totals and long prefix rows leave less margin
+// to the bf16 rounding of the outputs, at the cost of twice the O += P V
+// products on those tiles.
 template <int MODE, bool BF16, bool kSplitP, int NI>
 __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_t* wts, float c,
                                   float nmc, int hh, float& lsum, unsigned (&pk)[8],
@@ -572,18 +573,22 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   }
   wg_barrier();
   if (work) {
+    // Exact tiles of the proxy forward split their fp16 probabilities; its
+    // proxy tiles do not need to (their rounding moves the outputs far less
+    // than that of the exact tiles).
+    constexpr bool kSP = kProxy && MODE != kModeProxy;
     const float nmc = -st.mc;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int kh = kb0 + kb;
       unsigned pk[8], pl[8];
       if (MODE == kModeAny) {
-        if (px) half_probs<kModeProxy, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
-        else half_probs<kModePad, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        if (px) half_probs<kModeProxy, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        else half_probs<kModePad, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       } else {
-        half_probs<MODE, BF16, kProxy, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        half_probs<MODE, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
       }
-      pv_half<BF16, kProxy, NK2>(x.sv, kh, pk, pl, x.ln, x.hh, st);
+      pv_half<BF16, kSP, NK2>(x.sv, kh, pk, pl, x.ln, x.hh, st);
     }
     if (!BF16 && !kProxy) {
       // V operand reads run four MFMAs ahead, across both key halves
