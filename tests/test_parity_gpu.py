@@ -200,6 +200,41 @@ def test_degenerate_blocks(dev):
     assert g.ok(), str(g)
 
 
+def test_key_split_blocks_against_every_tile_kind(dev):
+    """Query blocks with at most 32 valid rows split each tile's keys between
+    the two waves, which keep separate running softmax states and merge them
+    at the end.  Every such block size (1, 8, 16, 17, 31, 32), next to full
+    blocks, attends to every cube: full, padded, half, half-padded and quarter
+    tiles, and one bf16 tile (a cube whose values are scaled by 2^-12, below
+    the range fp16 keeps exact).  Graded in full, with the row log-sum-exp,
+    in the default and in the shared-sweep order."""
+    rng = np.random.default_rng(41)
+    B, H = 1, 3
+    vbs = np.array([1, 8, 16, 17, 31, 32, 64, 40, 33, 20, 16, 5], np.int32)
+    nq = vbs.size
+    S = 64 * nq
+    q, k, v = (_rand_bf16(rng, (B, S, H, D)) for _ in range(3))
+    v[:, 64 * 7:64 * 8] = W.f32_to_bf16_bits(
+        (O.bf16_to_f64(v[:, 64 * 7:64 * 8]) * 2.0 ** -12).astype(np.float32))
+    topk = np.stack([rng.permutation(nq) for _ in range(B * H * nq)]).reshape(B, H, nq, nq)
+    topk = topk.astype(np.int32)
+    scale = np.float32(1 / math.sqrt(D))
+    args = [to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True), to_dev(topk, dev),
+            to_dev(vbs, dev)]
+    out, lse = vsa.vsa_fwd_lse(*args, float(scale))
+    shared = vsa.vsa_fwd(*args, float(scale), shared_sweep=True)
+    torch.cuda.synchronize()
+    o64 = O.vsa_fwd(q, k, v, topk, vbs, scale)
+    for name, o in (("default", from_dev(out)), ("shared sweep", from_dev(shared))):
+        g = grade_full(o, o64, vbs)
+        print(f"key-split blocks, {name}: {g}")
+        assert pad_rows_zero(o, vbs)
+        assert g.ok(), str(g)
+    items = [(0, h, c) for h in range(H) for c in range(nq)]
+    worst = _lse_check_items(lse.cpu().numpy(), q, k, topk, vbs, scale, items)
+    print(f"key-split blocks: max |d lse| / bound = {worst:.3g}")
+
+
 def test_all_keys_empty_row_is_zero(dev):
     rng = np.random.default_rng(22)
     B, H, nq = 1, 2, 4
