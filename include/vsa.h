@@ -82,7 +82,8 @@ const char* vsa_status_string(vsa_status s);
  * query cube's sweep over its KV cubes at a block taken from the GPU's
  * real-time counter, so that the query cubes of a head in flight at the same
  * time move through its K/V together and the XCD's L2 serves more of them
- * (config 2: about 4-6% less attention time, L2 hit rate 0.69 -> 0.80).  The
+ * (40 heads x 624 cubes, 78 per row: about 3-5% less attention time, L2 hit
+ * rate 0.68 -> 0.77; 40 x 1440 cubes, 180 per row: about 8% less).  The
  * result then depends on timing in the last bits of fp32 rounding, always
  * within the documented accuracy.
  */
@@ -133,7 +134,7 @@ vsa_status vsa_fwd(const void* q, const void* k, const void* v,
  * bytes (64 MiB) that the library holds on each GPU it runs on until the
  * process ends.  VSA_ERR_SCRATCH when the shape needs more than that, i.e.
  * when batch * num_heads * seq_len/64 tiles of 16 KB (plus one byte each,
- * 256-byte aligned) exceed it (about 4090 tiles: config 1's 8 x 84 fits, the
+ * 256-byte aligned) exceed it (about 4090 tiles: 8 heads x 84 cubes fit, the
  * 40 x 624 Wan2.2 shape does not).  The call allocates nothing and touches no
  * memory allocator.  Every call on one GPU shares that GPU's array, which is
  * fully rewritten by each call: calls that overlap in time on one GPU (two
