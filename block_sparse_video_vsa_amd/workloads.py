@@ -157,7 +157,7 @@ CONFIGS: dict[str, Config] = {
     "2": Config("2", 1, 40, (21, 30, 52), 78, True, True, False, 1002,
                 description="Wan2.2-A14B 832x480x81f: 21x30x52 grid, 624 cubes, H=40, topk=78"),
     "3a": Config("3a", 1, 40, (21, 30, 52), 78, True, True, True, 1003,
-                 description="config 2 plus a head-0 outlier stress (64 tokens, q and k x200)"),
+                 description="21x30x52 grid, 624 cubes, H=40, topk=78, plus a head-0 outlier stress (64 tokens, q and k x200)"),
     "3b": Config("3b", 1, 40, (21, 45, 80), 180, True, True, True, 1013,
                  description="1280x720x81f: 21x45x80 grid, 1440 cubes, H=40, topk=180, with outlier"),
     "4": Config("4", 1, 56, (21, 30, 52), 0, True, True, False, 1004, prefix_len=512, n_random=60,
