@@ -707,6 +707,31 @@ def test_lse_small_configs_full(dev, name):
     print(f"config {name}: max |d lse| / bound = {worst:.3g}")
 
 
+def test_lse_batch_two(dev):
+    """Row log-sum-exp with two batch entries of their own data and indices,
+    ragged and empty cubes: output equal to vsa_fwd, every row graded."""
+    rng = np.random.default_rng(92)
+    B, H, nblk, topk = 2, 3, 20, 6
+    vbs = rng.choice(np.array([64, 64, 33, 16, 1, 0], np.int32), size=nblk).astype(np.int32)
+    S = 64 * nblk
+    q, k = (_rand_bf16(rng, (B, S, H, D), 3.0) for _ in range(2))    # large logits, as the recipe
+    v = _rand_bf16(rng, (B, S, H, D))
+    topk_idx = np.argsort(rng.random((B, H, nblk, nblk)), axis=-1)[..., :topk].astype(np.int32)
+    args = [to_dev(q, dev, True), to_dev(k, dev, True), to_dev(v, dev, True), to_dev(topk_idx, dev),
+            to_dev(vbs, dev)]
+    scale = np.float32(1 / math.sqrt(D))
+    out, lse = vsa.vsa_fwd_lse(*args, float(scale))
+    plain = vsa.vsa_fwd(*args, float(scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), from_dev(plain))
+    o64, _ = O.vsa_fwd_lse(q, k, v, topk_idx, vbs, scale)
+    g = grade_full(from_dev(out), o64, vbs)
+    assert g.ok(), str(g)
+    items = [(b, h, c) for b in range(B) for h in range(H) for c in range(nblk)]
+    worst = _lse_check_items(lse.cpu().numpy(), q, k, topk_idx, vbs, scale, items)
+    print(f"batch two: max |d lse| / bound = {worst:.3g}")
+
+
 def test_lse_config2_sampled(dev):
     wl = workload("2")
     out, lse = vsa.vsa_fwd_lse(to_dev(wl.q, dev, True), to_dev(wl.k, dev, True),
@@ -1011,6 +1036,40 @@ def test_proxy_prefix_split_and_merge(dev):
     g = grade_full(out, o64, vbs)
     print(f"proxy prefix split: {g}")
     assert pad_rows_zero(out, vbs)
+    assert g.ok(), str(g)
+
+
+def test_proxy_batch_two(dev):
+    """Two batch entries with their own data and selections: 2 prefix + 110
+    video blocks, so each prefix query block runs as two sub-items merged per
+    (batch, head).  Block summaries bitwise, the padded call graded in full,
+    the bitmask and BSR calls bit-identical to it."""
+    rng = np.random.default_rng(91)
+    B, H, npb, nv = 2, 2, 2, 110
+    vbs = np.concatenate([[64, 48], rng.choice(np.array([64, 64, 64, 40, 17, 9, 0], np.int32),
+                                               size=nv)]).astype(np.int32)
+    S = 64 * vbs.size
+    q, k, v = (_rand_bf16(rng, (B, S, H, D)) for _ in range(3))
+    width = 10
+    sel = np.full((B, H, nv, width), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            for c in range(nv):
+                picks = rng.choice(nv, size=int(rng.integers(0, width + 1)), replace=False)
+                sel[b, h, c, :picks.size] = picks
+    dk, dv, dvbs = to_dev(k, dev, True), to_dev(v, dev, True), to_dev(vbs, dev)
+    km, vs = vsa.vsa_preprocess(dk, dv, dvbs)
+    km_o, vs_o = O.vsa_preprocess(k, v, vbs)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(km), km_o) and np.array_equal(from_dev(vs), vs_o)
+    scale = np.float32(1 / math.sqrt(D))
+    a, b_, c = _proxy_formats(dev, q, k, v, sel, vbs, 64 * npb, float(scale), True)
+    assert np.array_equal(a, b_), "bitmask differs from the padded selection"
+    assert np.array_equal(a, c), "BSR differs from the padded selection"
+    o64 = O.vsa_fwd_proxy(q, k, v, sel, vbs, km_o, vs_o, 64 * npb, scale)
+    g = grade_full(a, o64, vbs)
+    print(f"proxy batch two: {g}")
+    assert pad_rows_zero(a, vbs)
     assert g.ok(), str(g)
 
 
