@@ -24,7 +24,7 @@ constexpr int32_t kMaxHeads = 65536;      // one 64-row K cube of all heads stay
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t vt, pt, vf, pf, po, pl, total;
+  size_t vt, pt, vf, pf, po, pl, sc, total;
 };
 
 // Key blocks per prefix sub-item of the proxy forward: a prefix query block
@@ -36,6 +36,7 @@ int prefix_splits(int64_t nblk) { return (int)((nblk + kPrefixSplit - 1) / kPref
 
 // [V tiles B*H*nblk*16KB][proxy tiles B*H*nproxy*16KB][V flags][proxy flags]
 // [prefix partial O/l: B*H*nprefix*psplit*64*128 fp32][their lse: ... *64 fp32]
+// [tail-pool counters of the attention launch: kSchedBytes]
 WsLayout ws_layout(int64_t batch, int64_t heads, int64_t nblk, int64_t nproxy,
                    int64_t nprefix = 0, int64_t psplit = 0) {
   WsLayout l;
@@ -47,7 +48,8 @@ WsLayout ws_layout(int64_t batch, int64_t heads, int64_t nblk, int64_t nproxy,
   l.pf = align_up(l.vf + bh * (size_t)nblk, kWsAlign);
   l.po = align_up(l.pf + bh * (size_t)nproxy, kWsAlign);
   l.pl = align_up(l.po + subs * kBlock * kHeadDim * 4, kWsAlign);
-  l.total = align_up(l.pl + subs * kBlock * 4, kWsAlign);
+  l.sc = align_up(l.pl + subs * kBlock * 4, kWsAlign);
+  l.total = align_up(l.sc + kSchedBytes, kWsAlign);
   return l;
 }
 
@@ -167,6 +169,7 @@ vsa_status enqueue_attend(const void* q, const void* k, const int32_t* topk_idx,
   p.k = (const uint16_t*)k;
   p.vt = wsb + ws.vt;
   p.vt_flags = wsb + ws.vf;
+  p.sched = (int*)(wsb + ws.sc);
   p.idx = topk_idx;
   p.vbs = vbs;
   p.out = (uint16_t*)out;
@@ -265,14 +268,14 @@ extern "C" vsa_status vsa_fwd_prepacked_ex(const void* q, const void* k, const i
                                            const int32_t* vbs, void* out, int32_t batch,
                                            int32_t seq_len, int32_t num_heads, int32_t head_dim,
                                            int32_t topk, float sm_scale, uint32_t flags,
-                                           const void* workspace, size_t workspace_bytes,
+                                           void* workspace, size_t workspace_bytes,
                                            vsa_stream_t stream) {
   if (flags & ~(uint32_t)VSA_FLAG_SHARED_SWEEP) return VSA_ERR_VALUE;
   vsa_status st = check_fwd(q, k, nullptr, topk_idx, vbs, out, batch, seq_len, num_heads,
                             head_dim, topk, sm_scale, workspace, workspace_bytes, true, false);
   if (st != VSA_OK) return st;
   return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
-                        (void*)workspace, (hipStream_t)stream, nullptr, flags);
+                        workspace, (hipStream_t)stream, nullptr, flags);
 }
 
 extern "C" vsa_status vsa_fwd_lse(const void* q, const void* k, const void* v,
@@ -322,13 +325,13 @@ extern "C" vsa_status vsa_pack_values(const void* v, const int32_t* vbs, int32_t
 extern "C" vsa_status vsa_fwd_prepacked(const void* q, const void* k, const int32_t* topk_idx,
                                         const int32_t* vbs, void* out, int32_t batch,
                                         int32_t seq_len, int32_t num_heads, int32_t head_dim,
-                                        int32_t topk, float sm_scale, const void* workspace,
+                                        int32_t topk, float sm_scale, void* workspace,
                                         size_t workspace_bytes, vsa_stream_t stream) {
   vsa_status st = check_fwd(q, k, nullptr, topk_idx, vbs, out, batch, seq_len, num_heads,
                             head_dim, topk, sm_scale, workspace, workspace_bytes, true, false);
   if (st != VSA_OK) return st;
   return enqueue_attend(q, k, topk_idx, vbs, out, batch, seq_len, num_heads, topk, sm_scale,
-                        (void*)workspace, (hipStream_t)stream);
+                        workspace, (hipStream_t)stream);
 }
 
 extern "C" vsa_status vsa_preprocess(const void* k, const void* v, const int32_t* vbs,
@@ -454,6 +457,7 @@ vsa_status proxy_call(const void* q, const void* k, const void* v, const Selecti
   p.kmean = (const uint16_t*)kmean;
   p.vt = wsb + ws.vt;
   p.vt_flags = wsb + ws.vf;
+  p.sched = (int*)(wsb + ws.sc);
   p.pt = wsb + ws.pt;
   p.pt_flags = wsb + ws.pf;
   p.idx = sel.idx;

@@ -39,9 +39,10 @@
 // padding keys, half, half with padding keys, quarter), each kind through a
 // straight-line specialisation of the tile step, so the accumulators never
 // cross data-dependent control flow except the rescale.  Proxy and bf16 tiles
-// follow.  The start block comes from the workgroup's dispatch slot (the
-// default: every call gives the same bits) or, on request, from the real-time
-// counter (a shared sweep with better L2 reuse; see the kernel prologue).
+// follow.  The start block comes from the item's position in its XCD's run
+// (the default: every call gives the same bits) or, on request, from the
+// real-time counter (a shared sweep with better L2 reuse; see the kernel
+// prologue).
 #include "vsa_internal.h"
 
 #include <math.h>
@@ -665,9 +666,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // serves one head's K/V at a time.  A (batch, head) holds items_per_bh
   // items: its query blocks, or in proxy mode psplit sub-items per prefix
   // block (each over one range of pwidth key blocks) followed by the video
-  // blocks.
+  // blocks.  Tail balancing: the last kSchedPool items of each XCD's run are
+  // a pool.  The workgroups that reach it (plus kSchedExtra more per XCD)
+  // claim pool items through the XCDs' counters, their own XCD's first, so an
+  // XCD that runs ahead takes the last items of one that lags; a workgroup
+  // that finds every pool empty exits.  The item alone decides its result.
   const int xcd = (int)(blockIdx.x & 7);
-  const int item = xcd * p.items_per_xcd + (int)(blockIdx.x >> 3);
+  int iseq = (int)(blockIdx.x >> 3);     // position of the item in its XCD's run
+  int ixcd = xcd;
+  const int pool0 = p.items_per_xcd - kSchedPool;
+  if (p.sched != nullptr && pool0 > 0 && iseq >= pool0) {
+    __shared__ int s_claim;
+    if (tid == 0) {
+      int got = -1;
+      for (int d = 0; d < 8; ++d) {
+        const int y = (xcd + d) & 7;
+        const int j = __hip_atomic_fetch_add(p.sched + y * kSchedStride, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        if (j < kSchedPool) {
+          got = y * kSchedPool + j;
+          break;
+        }
+      }
+      s_claim = got;
+    }
+    __syncthreads();
+    const int got = s_claim;
+    if (got < 0) return;
+    ixcd = got / kSchedPool;
+    iseq = pool0 + got % kSchedPool;
+  } else if (iseq >= p.items_per_xcd) {
+    return;
+  }
+  const int item = ixcd * p.items_per_xcd + iseq;
   if (item >= p.n_items) return;
   const int bh = kProxy ? item / p.items_per_bh : item / p.nblk;
   const int ir = kProxy ? item - bh * p.items_per_bh : item % p.nblk;
@@ -794,10 +825,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int ncell = kKinds * nseg + 2;
   int* ccnt = sCell;                     // [ncell] tiles per cell
   int* cbeg = sCell + ncell;             // [ncell + 1] first position per cell
-  // Start block of the sweep.  Reproducible order: from the dispatch slot, so
-  // that the 128 workgroups resident on an XCD at once start spread evenly
-  // over the head's blocks (a slot's later items start where its first did),
-  // and the order depends on the shapes only.  Shared sweep (sweep_rate > 0):
+  // Start block of the sweep.  Reproducible order: from the item's position
+  // in its XCD's run, so that the 128 workgroups resident on an XCD at once
+  // start spread evenly over the head's blocks (a slot's later items start
+  // where its first did), and the order depends on the shapes only.  Shared sweep (sweep_rate > 0):
   // from the real-time counter, at sweep_rate blocks per tick, about the rate
   // at which a workgroup moves through its blocks; the resident workgroups of
   // a head then move through its blocks together, a narrow window of its K/V
@@ -807,7 +838,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const double pos = (double)__builtin_amdgcn_s_memrealtime() * (double)p.sweep_rate;
     start = (int)fmod(pos, (double)p.nblk);
   } else {
-    start = (int)(((int64_t)(blockIdx.x >> 3) * p.nblk / 128) % p.nblk);
+    start = (int)(((int64_t)iseq * p.nblk / 128) % p.nblk);
   }
   for (int t = tid; t < 2 * ncell + 1; t += kThreads) sCell[t] = 0;
   wg_barrier();
@@ -1025,6 +1056,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   store4(st.o3, 3);
 }
 
+// Zeroes the tail-pool counters before a launch (a kernel rather than a
+// memset node, so that captured graphs replay it like the other launches).
+__global__ void sched_reset_kernel(int* sched) {
+  if (threadIdx.x < 8) sched[threadIdx.x * kSchedStride] = 0;
+}
+
 }  // namespace
 
 size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
@@ -1049,8 +1086,15 @@ hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream)
   // about ten tiles of a typical item per sweep segment
   const int tiles = p.seg_tiles;
   p.nseg = std::min(kMaxSeg, std::max(1, (tiles + 5) / 10));
-  if (!launch_fits((int64_t)p.items_per_xcd * 8, kThreads)) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)p.items_per_xcd * 8u;
+  const bool balance = p.sched != nullptr && p.items_per_xcd > kSchedPool;
+  const int64_t per_xcd = (int64_t)p.items_per_xcd + (balance ? kSchedExtra : 0);
+  if (!launch_fits(per_xcd * 8, kThreads)) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(per_xcd * 8);
+  if (balance) {
+    hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.sched);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (proxy)
     hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, p);
   else

@@ -11,6 +11,15 @@ constexpr int kBlock = 64;       // tokens per cube / block
 constexpr int kHeadDim = 128;    // head geometry fixed at compile time
 constexpr int kTileBytes = kBlock * kHeadDim * 2;   // one 64 x 128 16-bit tile
 constexpr int kMaxSeg = 16;     // most sweep segments per item
+// Tail balancing of an attention launch: the last kSchedPool items of each
+// XCD's range form a pool, claimed through one agent-scope counter per XCD
+// (kSchedStride ints apart, one 256-byte line each) in the caller's
+// workspace; kSchedExtra more workgroups per XCD let a faster XCD take items
+// from the pools of slower ones.
+constexpr int kSchedPool = 256;
+constexpr int kSchedExtra = 128;
+constexpr int kSchedStride = 64;
+constexpr size_t kSchedBytes = 8 * kSchedStride * sizeof(int);
 // Work-items of one launch: the dispatch packet holds 32 bits; launches stay
 // at or below 2^31 so that a grid never truncates or overflows.
 constexpr int64_t kMaxLaunchThreads = (int64_t)1 << 31;
@@ -112,6 +121,7 @@ struct AttnParams {
   int pwidth;               // proxy: key blocks per prefix sub-item
   float* part_o;            // proxy: prefix partial outputs O/l [B*H][nprefix][psplit][64][128]
   float* part_lse;          // proxy: their row log-sum-exp [B*H][nprefix][psplit][64]
+  int* sched;               // kSchedBytes of tail-pool counters (workspace), or nullptr
 };
 
 hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream);

@@ -29,7 +29,8 @@
  *     nothing is enqueued and the status says why.  Data preconditions (indices
  *     in range and distinct per row, 0 <= vbs <= 64) are NOT checked on the
  *     device: an out-of-range index is skipped, a repeated index is counted twice.
- *   - Calls that share a workspace must not overlap in time.
+ *   - Calls that share a workspace must not overlap in time (every attention
+ *     call writes the workspace's scheduling counters).
  *   - Only head_dim == 128 is supported ([SH]; the head geometry is fixed at
  *     compile time, as in [RUN]).
  *   - Size limits (VSA_ERR_SHAPE otherwise): seq_len a positive multiple of 64
@@ -75,8 +76,10 @@ const char* vsa_status_string(vsa_status s);
  * Accumulation order.  By default the attention kernels visit each query
  * cube's KV tiles in an order that depends only on the shapes: repeated calls
  * with the same inputs give bitwise identical outputs, and the output does not
- * depend on the order of the entries of an index row.  The library holds no
- * mutable state between calls.
+ * depend on the order of the entries of an index row.  Which workgroup runs
+ * a query cube changes from call to call (the last ones are balanced across
+ * the XCDs at run time); its result does not.  The library holds no mutable
+ * state between calls.
  *
  * VSA_FLAG_SHARED_SWEEP (vsa_fwd_ex, vsa_fwd_prepacked_ex) instead starts each
  * query cube's sweep over its KV cubes at a block taken from the GPU's
@@ -92,7 +95,12 @@ const char* vsa_status_string(vsa_status s);
 /*
  * Workspace bytes vsa_fwd needs for this shape (0 if the shape is invalid).
  * The workspace holds each (batch, head, cube) V tile transposed to key-major
- * half precision, plus one byte per tile; it is fully rewritten by every call.
+ * half precision, plus one byte per tile, plus 2 KB of counters through which
+ * the attention launch balances its last work items across the XCDs.  The
+ * tiles are rewritten by every call that packs V (vsa_fwd, vsa_pack_values),
+ * the counters by every call that runs the attention (vsa_fwd_prepacked
+ * included), so even calls that only read the packed tiles must not overlap
+ * on one workspace.
  */
 size_t vsa_fwd_workspace_size(int32_t batch, int32_t seq_len, int32_t num_heads,
                               int32_t head_dim);
@@ -133,8 +141,8 @@ vsa_status vsa_fwd(const void* q, const void* k, const void* v,
  * packed V tiles go to a fixed scratch array of vsa_fwd_noalloc_max_bytes()
  * bytes (64 MiB) that the library holds on each GPU it runs on until the
  * process ends.  VSA_ERR_SCRATCH when the shape needs more than that, i.e.
- * when batch * num_heads * seq_len/64 tiles of 16 KB (plus one byte each,
- * 256-byte aligned) exceed it (about 4090 tiles: 8 heads x 84 cubes fit, the
+ * when batch * num_heads * seq_len/64 tiles of 16 KB (plus one byte each and
+ * 2 KB of counters, 256-byte aligned) exceed it (about 4090 tiles: 8 heads x 84 cubes fit, the
  * 40 x 624 Wan2.2 shape does not).  The call allocates nothing and touches no
  * memory allocator.  Every call on one GPU shares that GPU's array, which is
  * fully rewritten by each call: calls that overlap in time on one GPU (two
@@ -160,7 +168,7 @@ vsa_status vsa_fwd_prepacked_ex(const void* q, const void* k, const int32_t* top
                                 const int32_t* vbs, void* out,
                                 int32_t batch, int32_t seq_len, int32_t num_heads,
                                 int32_t head_dim, int32_t topk, float sm_scale, uint32_t flags,
-                                const void* workspace, size_t workspace_bytes,
+                                void* workspace, size_t workspace_bytes,
                                 vsa_stream_t stream);
 
 /*
@@ -181,7 +189,7 @@ vsa_status vsa_fwd_prepacked(const void* q, const void* k, const int32_t* topk_i
                              const int32_t* vbs, void* out,
                              int32_t batch, int32_t seq_len, int32_t num_heads, int32_t head_dim,
                              int32_t topk, float sm_scale,
-                             const void* workspace, size_t workspace_bytes, vsa_stream_t stream);
+                             void* workspace, size_t workspace_bytes, vsa_stream_t stream);
 
 /*
  * vsa_preprocess -- block summaries ([RUN] preprocess entry; [PX]).

@@ -46,9 +46,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # 16 KB packed V tile + one flag byte per (batch, head, cube), 256-byte aligned regions
+    # 16 KB packed V tile + one flag byte per (batch, head, cube), then 2 KB of
+    # tail-pool counters (eight, one 256-byte line each), 256-byte aligned regions
     n = native.fwd_workspace_size(1, 39936, 40)
-    assert n == 40 * 624 * 16384 + ((40 * 624 + 255) // 256) * 256
+    assert n == 40 * 624 * 16384 + ((40 * 624 + 255) // 256) * 256 + 2048
     assert native.fwd_workspace_size(2, 512, 2) >= 2 * 2 * 8 * 16384 + 32
     assert native.fwd_workspace_size(1, 100, 2) == 0
     assert native.fwd_workspace_size(1, 512, 2, 64) == 0
