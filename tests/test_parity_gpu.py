@@ -1073,6 +1073,52 @@ def test_proxy_batch_two(dev):
     assert g.ok(), str(g)
 
 
+def test_graph_replays_match_eager(dev):
+    """vsa_fwd on config 2 (its last items balanced across the XCDs through
+    workspace counters that a kernel zeroes) and vsa_fwd_noalloc on config 1,
+    each captured in a HIP graph: every replay, with eager work and
+    synchronisations between the replays, is bitwise the eager result."""
+    wl = workload("2")
+    q, k, v = (to_dev(x, dev, True) for x in (wl.q, wl.k, wl.v))
+    t, vbs = to_dev(wl.topk_idx, dev), to_dev(wl.vbs, dev)
+    B, S, H, _ = wl.q.shape
+    ws = torch.empty(vsa.fwd_workspace_size(B, S, H), dtype=torch.uint8, device=dev)
+    scale = float(wl.sm_scale)
+    eager = vsa.vsa_fwd(q, k, v, t, vbs, scale, workspace=ws).clone()
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vsa.vsa_fwd(q, k, v, t, vbs, scale, out=out, workspace=ws)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        vsa.vsa_fwd(q, k, v, t, vbs, scale, workspace=ws)    # eager use of the same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"vsa_fwd replay {rep}"
+    del q, k, v, ws, out, eager, g
+    wl1 = W.generate("1")
+    q1, k1, v1 = (to_dev(x, dev, True) for x in (wl1.q, wl1.k, wl1.v))
+    t1, vbs1 = to_dev(wl1.topk_idx, dev), to_dev(wl1.vbs, dev)
+    eager1 = vsa.vsa_fwd_noalloc(q1, k1, v1, t1, vbs1, torch.empty_like(q1), float(wl1.sm_scale))
+    wl0 = W.generate("0")
+    q0, k0, v0 = (to_dev(x, dev, True) for x in (wl0.q, wl0.k, wl0.v))
+    t0, vbs0 = to_dev(wl0.topk_idx, dev), to_dev(wl0.vbs, dev)
+    out0 = torch.empty_like(q0)
+    out1 = torch.empty_like(q1)
+    torch.cuda.synchronize()
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        vsa.vsa_fwd_noalloc(q1, k1, v1, t1, vbs1, out1, float(wl1.sm_scale))
+    for rep in range(3):
+        out1.fill_(float("nan"))
+        vsa.vsa_fwd_noalloc(q0, k0, v0, t0, vbs0, out0, float(wl0.sm_scale))   # rewrites the scratch
+        torch.cuda.synchronize()
+        g1.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out1.view(torch.int16), eager1.view(torch.int16)), f"noalloc replay {rep}"
+
+
 def test_concurrent_streams_get_their_own_workspace(dev):
     """Two calls enqueued on two streams with no synchronisation between them
     (different inputs, same shapes) each equal their single-stream result bit
