@@ -69,6 +69,9 @@ constexpr int kThreads = 128;
 // many log2 units, so probabilities stay below 2^8 (well inside fp16's range)
 // while tiles whose maximum grew only a little skip the accumulator rescale.
 constexpr float kRescaleSlack = 8.0f;
+// Exact tiles of the proxy forward keep single fp16 probabilities when all of
+// them are below 2^-kLowPartSkip (log2 units below the running maximum).
+constexpr float kLowPartSkip = 10.0f;
 
 
 // Tile-table entry: block/tile id (bits 0-19), valid rows (20-26), bf16 V (27),
@@ -328,10 +331,10 @@ __device__ inline float proxy_weight(const uint8_t* wts, int kb, int i, int hh) 
 // by more than kRescaleSlack.
 // NI registers of each 32-key half take part: 16, or 8 (keys 0-15) for
 // quarter tiles, whose keys 16-31 are not loaded.  s[kb] holds key half
-// kb0 + kb.
+// kb0 + kb.  Returns the lane's tile maximum.
 template <int NKB, int NI, int MODE>
-__device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts, float c, int hh,
-                                State& st, int kb0) {
+__device__ inline float tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts, float c, int hh,
+                                 State& st, int kb0) {
   float t = -INFINITY;
   if (MODE == kModeProxy) {
     // a proxy logit is offset by log2 of its weight (-inf for weight 0)
@@ -365,6 +368,7 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
     st.o2 *= alpha;
     st.o3 *= alpha;
   }
+  return t;
 }
 
 // Probabilities of one 32-key half (register i = key 32kb + 8(i/4) + 4hh + i%4)
@@ -378,10 +382,11 @@ __device__ inline void tile_max(const f32x16 (&s)[2], int nv, const uint8_t* wts
 // probabilities (relative 2^-12 each); the proxy forward splits those of its
 // exact tiles, because its value totals and long prefix rows leave less margin
 // to the bf16 rounding of the outputs, at the cost of twice the O += P V
-// products on those tiles.
+// products on those tiles (skipped where all of a tile's probabilities are
+// tiny, see tile_step).
 template <int MODE, bool BF16, bool kSplitP, int NI>
 __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_t* wts, float c,
-                                  float nmc, int hh, float& lsum, unsigned (&pk)[8],
+                                  float nmc, int hh, bool lo, float& lsum, unsigned (&pk)[8],
                                   unsigned (&pl)[8]) {
   auto keyw = [&](int i) { return proxy_weight(wts, kb, i, hh); };
   auto prob = [&](int i) {
@@ -403,6 +408,7 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
     }
   } else {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    const unsigned lomask = lo ? 0xFFFFFFFFu : 0u;   // low parts zero when they are skipped
 #pragma unroll
     for (int i = 0; i < NI; i += 2) {
       const float p0 = prob(i), p1 = prob(i + 1);
@@ -414,7 +420,7 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
       pk[i / 2] = __builtin_bit_cast(unsigned, h);
       lsum = __builtin_amdgcn_fdot2(h, wv, lsum, false);
       if (kSplitP) {
-        pl[i / 2] = f16_low_part(pk[i / 2], p0, p1);
+        pl[i / 2] = f16_low_part(pk[i / 2], p0, p1) & lomask;
         lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pl[i / 2]), wv, lsum, false);
       }
     }
@@ -428,7 +434,7 @@ __device__ inline void half_probs(const f32x16& sk, int kb, int nv, const uint8_
 // bf16 tiles run each step twice, with the high and the low probability parts.
 template <bool BF16, bool kSplitP, int NK2>
 __device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (&pk)[8],
-                               const unsigned (&pl)[8], int ln, int hh, State& st) {
+                               const unsigned (&pl)[8], bool lo, int ln, int hh, State& st) {
   const int chunk = (hh ^ vt_swizzle(ln)) << 4;
 #pragma unroll
   for (int k2 = 0; k2 < NK2; ++k2) {
@@ -448,26 +454,24 @@ __device__ inline void pv_half(const unsigned char* sv, int kb, const unsigned (
       VSA_PV_BF16(st.o2, 2)
       VSA_PV_BF16(st.o3, 3)
 #undef VSA_PV_BF16
-    } else if (kSplitP) {
-      const u32x4 lb = {pl[4 * k2], pl[4 * k2 + 1], pl[4 * k2 + 2], pl[4 * k2 + 3]};
-      const f16x8 bh = __builtin_bit_cast(f16x8, pb), bl = __builtin_bit_cast(f16x8, lb);
-#define VSA_PV_F16(acc, db)                                                           \
-      {                                                                               \
-        const f16x8 a = *(const f16x8*)(vb + (db) * 1024);                            \
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh, acc, 0, 0, 0);            \
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl, acc, 0, 0, 0);            \
-      }
-      VSA_PV_F16(st.o0, 0)
-      VSA_PV_F16(st.o1, 1)
-      VSA_PV_F16(st.o2, 2)
-      VSA_PV_F16(st.o3, 3)
-#undef VSA_PV_F16
     } else {
       const f16x8 bb = __builtin_bit_cast(f16x8, pb);
       st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 1024), bb, st.o0, 0, 0, 0);
       st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 1024), bb, st.o1, 0, 0, 0);
       st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 1024), bb, st.o2, 0, 0, 0);
       st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 1024), bb, st.o3, 0, 0, 0);
+    }
+  }
+  if (!BF16 && kSplitP && lo) {
+    // the low parts of split fp16 probabilities, with the V operand read again
+#pragma unroll
+    for (int k2 = 0; k2 < NK2; ++k2) {
+      const unsigned char* vb = sv + kb * 8192 + k2 * 4096 + ln * 32 + chunk;
+      const f16x8 bl = __builtin_bit_cast(f16x8, (u32x4){pl[4 * k2], pl[4 * k2 + 1], pl[4 * k2 + 2], pl[4 * k2 + 3]});
+      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 0 * 1024), bl, st.o0, 0, 0, 0);
+      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 1 * 1024), bl, st.o1, 0, 0, 0);
+      st.o2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 2 * 1024), bl, st.o2, 0, 0, 0);
+      st.o3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)(vb + 3 * 1024), bl, st.o3, 0, 0, 0);
     }
   }
 }
@@ -486,6 +490,7 @@ struct Ctx {
   uint32_t row_bytes, klane, vlane;
   int w, lane, ln, hh, tid;
   float c;
+  bool qv;                 // this lane's query row is a valid token
 };
 
 template <bool kProxy>
@@ -553,13 +558,23 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   // The running max, the probabilities and O += P V run at raised wave
   // priority: where both waves of a SIMD can issue, this phase goes first.
   __builtin_amdgcn_s_setprio(2);
+  // Exact fp16 tiles of the proxy forward split their probabilities; its
+  // proxy tiles do not need to (their rounding moves the outputs far less
+  // than that of the exact tiles).  An exact tile whose probabilities are
+  // all below 2^-kLowPartSkip in every valid query row of the wave keeps
+  // single ones: their low parts are below 2^-(kLowPartSkip + 12) of the
+  // running maximum's term.
+  constexpr bool kSP = kProxy && MODE != kModeProxy && !BF16;
+  bool split = kSP;
   if (work) {
+    float tmax;
     if (MODE == kModeAny) {
-      if (px) tile_max<NKB, NI, kModeProxy>(s, nv, wts, x.c, x.hh, st, kb0);
-      else tile_max<NKB, NI, kModePad>(s, nv, wts, x.c, x.hh, st, kb0);
+      if (px) tmax = tile_max<NKB, NI, kModeProxy>(s, nv, wts, x.c, x.hh, st, kb0);
+      else tmax = tile_max<NKB, NI, kModePad>(s, nv, wts, x.c, x.hh, st, kb0);
     } else {
-      tile_max<NKB, NI, MODE>(s, nv, wts, x.c, x.hh, st, kb0);
+      tmax = tile_max<NKB, NI, MODE>(s, nv, wts, x.c, x.hh, st, kb0);
     }
+    if (kSP) split = __ballot(x.qv && tmax >= st.mc - kLowPartSkip) != 0ull;
   }
 
   // V(j) has landed once only K(j+1)'s copies may still be in flight.
@@ -574,22 +589,18 @@ __device__ inline void tile_step(const Ctx& x, const bf16x8 (&qop)[8], State& st
   }
   wg_barrier();
   if (work) {
-    // Exact tiles of the proxy forward split their fp16 probabilities; its
-    // proxy tiles do not need to (their rounding moves the outputs far less
-    // than that of the exact tiles).
-    constexpr bool kSP = kProxy && MODE != kModeProxy;
     const float nmc = -st.mc;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int kh = kb0 + kb;
       unsigned pk[8], pl[8];
       if (MODE == kModeAny) {
-        if (px) half_probs<kModeProxy, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
-        else half_probs<kModePad, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        if (px) half_probs<kModeProxy, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, split, st.lsum, pk, pl);
+        else half_probs<kModePad, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, split, st.lsum, pk, pl);
       } else {
-        half_probs<MODE, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, st.lsum, pk, pl);
+        half_probs<MODE, BF16, kSP, NI>(s[kb], kh, nv, wts, x.c, nmc, x.hh, split, st.lsum, pk, pl);
       }
-      pv_half<BF16, kSP, NK2>(x.sv, kh, pk, pl, x.ln, x.hh, st);
+      pv_half<BF16, kSP, NK2>(x.sv, kh, pk, pl, split, x.ln, x.hh, st);
     }
     if (!BF16 && !kProxy) {
       // V operand reads run four MFMAs ahead, across both key halves
@@ -947,6 +958,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   x.hh = hh;
   x.tid = tid;
   x.c = p.c;
+  x.qv = qrow < vq;
   State st;
   st.o0 = f32x16{};
   st.o1 = f32x16{};
