@@ -122,6 +122,7 @@ struct AttnParams {
   float* part_o;            // proxy: prefix partial outputs O/l [B*H][nprefix][psplit][64][128]
   float* part_lse;          // proxy: their row log-sum-exp [B*H][nprefix][psplit][64]
   int* sched;               // kSchedBytes of tail-pool counters (workspace), or nullptr
+  int zero_skip;            // skip fp16 tiles whose probabilities all round to 0 (set at launch)
 };
 
 hipError_t launch_pack(const PackParams& p, int batch, hipStream_t stream);
