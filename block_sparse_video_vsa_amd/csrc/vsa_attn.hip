@@ -1099,14 +1099,11 @@ size_t attn_dyn_lds(const AttnParams& p, bool proxy) {
 hipError_t launch_attn(const AttnParams& params, bool proxy, hipStream_t stream) {
   if (params.n_items <= 0) return hipSuccess;
   AttnParams p = params;
-  // Shared sweep: the clock moves through a head's blocks at nblk / (tiles *
-  // kTicksPerTile) per tick of the 100 MHz real-time counter.  A workgroup
-  // crosses a 64-key tile in about 1.75 us (40 heads x 624 cubes) to 2.0 us
-  // (40 x 1440 cubes) on MI355X; a clock a little ahead of that pace keeps
-  // the workgroups of a head together best (180 ticks: 2.5% faster than 200
-  // on the larger shape), while a much faster one scatters them (160 ticks:
-  // 23% slower there).
-  constexpr float kTicksPerTile = 180.0f;
+  // Shared sweep: a workgroup crosses about one tile per kTicksPerTile ticks of
+  // the 100 MHz real-time counter (MI355X, configs 2 and 3b: 2.0-2.2 us per
+  // 64-key tile per workgroup), so its blocks pass at nblk / (tiles *
+  // kTicksPerTile) per tick.
+  constexpr float kTicksPerTile = 200.0f;
   if (p.sweep_rate > 0.0f)
     p.sweep_rate = (float)p.nblk / ((float)std::max(1, p.seg_tiles) * kTicksPerTile);
   const size_t dyn = attn_dyn_lds(p, proxy);
